@@ -1,0 +1,201 @@
+"""Benchmark of the ISD verify-and-propose step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c64] [--sigma-index 1]
+
+One step = isd_paged_attn over the whole batch (one attention layer) followed
+by isd_accept for the whole batch, on one stream, inputs resident in HBM.
+Default workload: B = 64 sequences (C = 64), N = 4, 32 query / 8 KV heads,
+D = 128, bf16 KV in 16-token pages, contexts ~ U[2048, 16384], vocab 151936,
+logit perturbation sigma = 0.5, T = 1.
+
+Prints one JSON line with steps/s (``value``), committed and accepted-draft
+tokens/s, per-kernel times from HIP events recorded on the launch stream
+inside the timed region, the attention kernel's roofline against 8 TB/s and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+import os
+
+# The CPU baseline is the single-threaded oracle; pin BLAS before numpy loads.
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, "1")
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
+
+import numpy as np  # noqa: E402
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def attn_bytes(w):
+    """Algorithmic HBM bytes of one attention launch: every K and V element of
+    every context once, Q once, O once, and the page-table entries used."""
+    es = 2 if w.qkv_dtype == "bf16" else 4
+    tok = int(w.ctx_lens.astype(np.int64).sum())
+    pages = int(((w.ctx_lens.astype(np.int64) + 15) // 16).sum())
+    kv = tok * w.Hkv * w.D * 2 * es
+    qo = 2 * w.B * w.R * w.Hq * w.D * es
+    return kv + qo + pages * w.Hkv * 4
+
+
+def accept_bytes(w, lens, kp):
+    """Algorithmic HBM bytes of one acceptance launch pair: all 2N-1 logit rows
+    once, then the residual pair (p_j and q_j rows) or the bonus row once."""
+    es = 2 if w.logits_dtype == "bf16" else 4
+    rows = w.B * w.R
+    resid = int(((lens - 1) < kp).sum())
+    bonus = w.B - resid
+    return (rows + 2 * resid + bonus) * w.V * es + w.B * (w.N + 1) * 4
+
+
+def cpu_baseline(w, n_seq):
+    """Time the oracle on the first ``n_seq`` sequences and scale to the batch."""
+    from oracle.accept import isd_accept
+    from oracle.attention import isd_attention
+    from oracle.dtypes import to_f64
+
+    sub = slice(0, n_seq)
+    q = to_f64(w.q[sub], w.qkv_dtype).reshape(w.q[sub].shape)
+    t0 = time.perf_counter()
+    isd_attention(q, w.kv_pages, w.page_table[sub], w.ctx_lens[sub], w.N, w.Hkv, w.qkv_dtype)
+    t1 = time.perf_counter()
+    isd_accept(w.logits_clean[sub], w.logits_mask[sub], w.draft_tokens[sub], w.seed, w.T,
+               dtype=w.logits_dtype)
+    t2 = time.perf_counter()
+    tok_all = float(w.ctx_lens.sum())
+    tok_sub = float(w.ctx_lens[sub].sum())
+    est = (t1 - t0) * tok_all / tok_sub + (t2 - t1) * w.B / n_seq
+    return {
+        "value": 1.0 / est,
+        "unit": "ISD steps/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n_seq} of {w.B} sequences ({int(tok_sub)} of {int(tok_all)} context "
+                  f"tokens): attention {t1 - t0:.2f} s scaled by context tokens, acceptance "
+                  f"{t2 - t1:.2f} s scaled by sequences; single thread, float64 numpy",
+        "step_seconds_estimated": est,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c64")
+    ap.add_argument("--sigma-index", type=int, default=1)
+    ap.add_argument("--cpu-sample", type=int, default=4, help="sequences timed on the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the step shards over "
+              "sequences with no exchange, so per-GPU throughput is the one-GPU figure.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from speculative_verify_isd_amd import workloads
+    from speculative_verify_isd_amd.lib import DeviceStep
+
+    w = workloads.named_workload(args.workload, args.sigma_index)
+    ds = DeviceStep(w)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        ds.attn()
+        ds.accept(debug=False)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        ds.attn()
+        ev[k][1].record(stream)
+        ds.accept(debug=False)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]))
+    acc_ms = float(np.mean([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]))
+    span_ms = ev[0][0].elapsed_time(ev[K - 1][2])
+    ms_per_step = span_ms / K
+
+    lens = ds.lens.cpu().numpy()
+    kp = (w.draft_tokens >= 0).sum(axis=1) if w.N > 1 else np.zeros(w.B, dtype=np.int64)
+    committed = int(lens.sum())
+    a_bytes = attn_bytes(w)
+    c_bytes = accept_bytes(w, lens, kp)
+    attn_gbs = a_bytes / (attn_ms * 1e-3) / 1e9
+    acc_gbs = c_bytes / (acc_ms * 1e-3) / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "isd_paged_attn_c64_traffic.json")
+    if os.path.exists(tfile):
+        try:
+            traffic = json.load(open(tfile)).get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": "ISD steps/s + accepted tok/s at C=64, N=4; % of HBM roofline (rocprof)",
+        "value": 1000.0 / ms_per_step,
+        "unit": "ISD steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy: N(0,1) Q/K/V, N(0,3^2) logits with N(0,sigma^2) "
+                "clean-row perturbation, drafts drawn from q)",
+        "config": {
+            "workload": f"{w.name}: B={w.B} (C={w.B}), N={w.N}, Hq/Hkv={w.Hq}/{w.Hkv}, D={w.D}, "
+                        f"bf16 KV in 16-token pages, ctx U[2048,16384] (sum {int(w.ctx_lens.sum())}), "
+                        f"V={w.V}, sigma={w.meta['sigma']}, T={w.T}, one attention layer",
+            "global_batch": w.B,
+            "N": w.N,
+            "parallelism": "single GPU",
+        },
+        "committed_tok_per_s": committed * 1000.0 / ms_per_step,
+        "accepted_draft_tok_per_s": (committed - w.B) * 1000.0 / ms_per_step,
+        "mean_accept_len": committed / w.B,
+        "kernels": {
+            "isd_paged_attn": {"ms": attn_ms, "algorithmic_bytes": a_bytes, "GB/s": attn_gbs,
+                               "frac_of_8TB/s": attn_gbs / HBM_PEAK_GBS},
+            "isd_accept": {"ms": acc_ms, "algorithmic_bytes": c_bytes, "GB/s": acc_gbs,
+                           "frac_of_8TB/s": acc_gbs / HBM_PEAK_GBS},
+        },
+        "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic},
+        "host_wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

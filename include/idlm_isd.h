@@ -1,0 +1,175 @@
+/*
+ * idlm_isd.h -- C ABI of libidlm_isd.so, the MI355X (gfx950) ISD step.
+ *
+ * One Introspective Strided Decoding (ISD) step verifies the previous
+ * step's drafts and proposes new ones in a single forward.  The library
+ * implements the data-parallel part of that step on one GPU:
+ *
+ *   1. idlm_isd_paged_attn: strictly causal grouped-query attention of the
+ *      2N-1 step rows of every sequence over a paged KV cache.  Causal
+ *      attention over all positions is what lets the model run in an
+ *      autoregressive serving stack ("Introspective Diffusion Language
+ *      Models", sections "Training" and "Serving (SGLang)"); a forward
+ *      carries 2N-1 queries (section "How do DLMs perform as they approach
+ *      compute-bound?"); the cache is paged ("Serving (SGLang)").
+ *   2. idlm_isd_accept: the acceptance stage.  Clean rows give the anchor
+ *      distribution p, MASK rows the proposal distribution q; draft x is
+ *      kept with probability min(1, p(x)/q(x)), the first rejection is
+ *      resampled from normalize(max(0, p - q)), and the committed prefix is
+ *      truncated there ("Introspective Diffusion Language Models", section
+ *      "Inference & ISD"; GeekNews summary, section "Inference & ISD").
+ *   3. idlm_isd_step: 1 then 2 on one stream.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked [device] are caller-owned device memory; [host] are
+ *   caller-owned host memory, read during the call only.  The library
+ *   allocates nothing; per-call scratch lives in the caller's workspace.
+ * - Everything is enqueued on `stream` (a hipStream_t passed as void*;
+ *   NULL = the default stream) and returns without synchronising, except
+ *   idlm_isd_read_status.
+ * - A nonzero return is an idlm_status; nothing was enqueued when a call
+ *   fails host-side validation.  Host validation needs no GPU.
+ * - Bad *device data* (a page id outside [0, num_pages), a context length
+ *   outside [2N-1, 16*max_pages], a draft id outside [-1, V)) cannot be seen
+ *   on the host: kernels clamp the value, set a sticky status word in the
+ *   workspace and leave that sequence's outputs unspecified.  Read it with
+ *   idlm_isd_read_status.
+ * - Calls on one workspace must not overlap (they share its counters); use
+ *   one workspace per concurrent stream.
+ *
+ * Symbols: B batch, N stride, R = 2N-1 query rows, K = N-1 drafts, Hq / Hkv
+ * query / KV heads, G = Hq/Hkv, D head dim, V vocabulary, P pool pages.
+ *
+ * Paged KV layout
+ * ---------------
+ * kv_pages is [P][2][Hkv][16*D] elements of qkv_dtype: for every physical
+ * page a K block ([.][0][h]) and a V block ([.][1][h]) per KV head, each
+ * holding 16 token slots.
+ *   K block: 16-byte column chunks.  With x = 16 / sizeof(element) (8 for
+ *            bf16, 4 for f32), (slot s, dim d) is at ((d/x)*16 + s)*x + d%x.
+ *   V block: transposed, (slot s, dim d) is at d*16 + s.
+ * Logical token t of sequence b is slot t%16 of page page_table[b][t/16].
+ * ctx_lens[b] counts the R new rows, whose K/V the caller has already
+ * written; step row r sits at position ctx_lens[b]-R+r and attends to tokens
+ * 0..ctx_lens[b]-R+r.  Scores are q.k/sqrt(D); query head h reads KV head
+ * h/G; q and k arrive with rotary embedding applied.
+ */
+#ifndef IDLM_ISD_H
+#define IDLM_ISD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { IDLM_BF16 = 0, IDLM_F32 = 1 } idlm_dtype;
+
+typedef enum {
+  IDLM_OK = 0,
+  IDLM_ERR_NULL = 1,        /* a required pointer is NULL */
+  IDLM_ERR_DIMS = 2,        /* a size is out of range or inconsistent */
+  IDLM_ERR_UNSUPPORTED = 3, /* valid but not built: D, dtype or tile shape */
+  IDLM_ERR_TEMPERATURE = 4, /* T < 0 or not finite */
+  IDLM_ERR_WORKSPACE = 5,   /* workspace too small or misaligned */
+  IDLM_ERR_HIP = 6,         /* a HIP runtime call failed */
+  IDLM_ERR_DEVICE_DATA = 7  /* kernels saw bad device data (read_status) */
+} idlm_status;
+
+/* Sizes of one step.  Passed by [host] pointer. */
+typedef struct {
+  int32_t B;            /* sequences, >= 0 (0 is a no-op)                    */
+  int32_t N;            /* stride, 1..16; R = 2N-1 rows, K = N-1 drafts      */
+  int32_t Hq, Hkv;      /* query / KV heads; Hq % Hkv == 0; R*Hq/Hkv <= 128  */
+  int32_t D;            /* head dim: 64 or 128                               */
+  int32_t V;            /* vocabulary, >= 1                                  */
+  int32_t page_size;    /* tokens per page: must be 16                       */
+  int32_t max_pages;    /* row stride of page_table, >= 1                    */
+  int32_t num_pages;    /* pages in the pool (device range check), >= 1     */
+  int32_t qkv_dtype;    /* idlm_dtype of q, kv_pages and attn_out            */
+  int32_t logits_dtype; /* idlm_dtype of logits_clean and logits_mask        */
+} idlm_isd_dims;
+
+/* Bytes of workspace every entry point below needs for these sizes; 0 for
+ * invalid sizes.  Host only. */
+size_t idlm_isd_workspace_bytes(const idlm_isd_dims* d);
+
+/* Check sizes and temperature without touching the GPU.  Returns IDLM_OK,
+ * IDLM_ERR_NULL, IDLM_ERR_DIMS, IDLM_ERR_UNSUPPORTED or
+ * IDLM_ERR_TEMPERATURE.  Host only. */
+int32_t idlm_isd_validate(const idlm_isd_dims* d, float T);
+
+/* Prepare a workspace for first use: clears its counters and status word
+ * with a fill kernel on `stream`.  Must run once after allocating (or after
+ * any foreign write to) the workspace; the step kernels return every counter
+ * to zero themselves. */
+int32_t idlm_isd_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/* Causal paged GQA attention of the R step rows (see the header comment).
+ *   q          [device] [B][R][Hq][D] qkv_dtype
+ *   kv_pages   [device] [P][2][Hkv][16*D] qkv_dtype, layout above
+ *   page_table [device] int32 [B][max_pages]
+ *   ctx_lens   [device] int32 [B]
+ *   attn_out   [device] [B][R][Hq][D] qkv_dtype, written
+ * bf16 runs bf16 MFMA with float32 accumulation and softmax; f32 runs float32
+ * FMA.  Output rows are the softmax-weighted sums rounded once to
+ * qkv_dtype. */
+int32_t idlm_isd_paged_attn(const idlm_isd_dims* d, const void* q, const void* kv_pages,
+                            const int32_t* page_table, const int32_t* ctx_lens, void* attn_out,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Acceptance stage.
+ *   logits_clean   [device] [B][N][V] logits_dtype.  Clean row i (i < K)
+ *                  gives p_i, which verifies draft i; row K gives the bonus
+ *                  distribution used when every draft is kept.
+ *   logits_mask    [device] [B][K][V] logits_dtype.  MASK row i gives q_i,
+ *                  the distribution draft i was proposed from.  May be NULL
+ *                  when N == 1.
+ *   draft_tokens   [device] int32 [B][K]; a -1 ends sequence b's list early
+ *                  (k < K drafts; the bonus then comes from clean row k).
+ *                  May be NULL when N == 1.
+ *   seed           Philox4x64-10 key word 0; key word 1 is b; counter
+ *                  (i,0,0,0) gives u_i (word 0, ratio test) and u'_i (word 1,
+ *                  sampling) as (word >> 40) * 2^-24.
+ *   T              temperature >= 0; p = softmax(clean/T), q = softmax(mask/T);
+ *                  T == 0 is greedy (one-hot argmax, lowest index on ties).
+ *   out_tokens     [device] int32 [B][N]: kept drafts, then the resampled or
+ *                  bonus token, then -1 padding.
+ *   out_accept_len [device] int32 [B]: tokens committed, in 1..N.
+ *   out_debug      [device] double [B][N+1][4] or NULL.  Row i < N holds
+ *                  (p_i(x_i), q_i(x_i), u_i, u'_i) for every draft tested
+ *                  (NaN elsewhere); row N holds (sum of sampling weights,
+ *                  threshold t, u' used, committed token).
+ * Draft i is kept iff p_i(x) >= q_i(x) or u_i*q_i(x) < p_i(x), both in
+ * float64.  At the first rejected index j the token is the smallest v whose
+ * running sum of w = max(0, p_j - q_j) exceeds t = u'_j * sum(w) (sum(w) == 0
+ * falls back to w = p_j); with no rejection w = p_k (bonus row). */
+int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const void* logits_mask,
+                        const int32_t* draft_tokens, uint64_t seed, float T, int32_t* out_tokens,
+                        int32_t* out_accept_len, double* out_debug, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/* One ISD step: idlm_isd_paged_attn then idlm_isd_accept on `stream`.  N
+ * must equal d->N (it is repeated to keep the step's own argument list). */
+int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
+                      const int32_t* page_table, const int32_t* ctx_lens,
+                      const void* logits_clean, const void* logits_mask,
+                      const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
+                      int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/* Synchronise `stream`, then copy the workspace's sticky device status into
+ * *host_code (IDLM_OK or IDLM_ERR_DEVICE_DATA).  Cleared only by
+ * idlm_isd_workspace_init. */
+int32_t idlm_isd_read_status(const void* workspace, void* stream, int32_t* host_code);
+
+/* Static description of a status code. */
+const char* idlm_isd_strerror(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDLM_ISD_H */

@@ -1,0 +1,230 @@
+// C ABI of libidlm_isd.so: host validation, workspace planning and dispatch.
+// Validation and planning are plain host code and never touch the GPU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "isd_internal.hpp"
+
+namespace idlm {
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int32_t check_dims(const idlm_isd_dims* d) {
+  if (!d) return IDLM_ERR_NULL;
+  if (d->B < 0 || d->B > (1 << 24)) return IDLM_ERR_DIMS;
+  if (d->N < 1 || d->N > 16) return IDLM_ERR_DIMS;
+  if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return IDLM_ERR_DIMS;
+  if (d->V < 1 || d->page_size < 1 || d->max_pages < 1 || d->num_pages < 1) return IDLM_ERR_DIMS;
+  if ((int64_t)d->max_pages * 16 > (1ll << 30)) return IDLM_ERR_DIMS;
+  if (d->qkv_dtype != IDLM_BF16 && d->qkv_dtype != IDLM_F32) return IDLM_ERR_DIMS;
+  if (d->logits_dtype != IDLM_BF16 && d->logits_dtype != IDLM_F32) return IDLM_ERR_DIMS;
+  if (d->page_size != kPage) return IDLM_ERR_UNSUPPORTED;
+  if (d->D != 64 && d->D != 128) return IDLM_ERR_UNSUPPORTED;
+  const int64_t R = 2 * (int64_t)d->N - 1;
+  if (R * (d->Hq / d->Hkv) > 128) return IDLM_ERR_UNSUPPORTED;
+  if ((int64_t)d->B * d->Hkv > (1 << 24)) return IDLM_ERR_DIMS;
+  return IDLM_OK;
+}
+
+int32_t check_T(float T) {
+  if (!(T >= 0.0f) || !isfinite(T)) return IDLM_ERR_TEMPERATURE;
+  return IDLM_OK;
+}
+
+int pow2_floor(int64_t x) {
+  int p = 1;
+  while ((int64_t)p * 2 <= x) p *= 2;
+  return p;
+}
+
+}  // namespace
+
+bool make_plan(const idlm_isd_dims& d, Plan* p) {
+  if (check_dims(&d) != IDLM_OK) return false;
+  memset(p, 0, sizeof(*p));
+  // ---- attention ----
+  AttnPlan& a = p->attn;
+  a.R = 2 * d.N - 1;
+  a.G = d.Hq / d.Hkv;
+  a.RG = a.R * a.G;
+  a.WR = a.RG <= 32 ? 1 : (a.RG <= 64 ? 2 : 4);
+  a.RGp = 32 * a.WR;
+  a.npairs = d.B * d.Hkv;
+  // Chunk so that a full batch gives ~2048 work-groups, within [8, cap] pages;
+  // larger query tiles get longer chunks so their fp32 partials stay a few
+  // percent of the KV bytes they summarise.
+  const int cap = a.WR == 1 ? 64 : 256;
+  const int64_t want = ((int64_t)a.npairs * d.max_pages) / 2048;
+  a.CP = (int)std::min<int64_t>(cap, std::max<int64_t>(8, pow2_floor(std::max<int64_t>(want, 1))));
+  a.maxc = (int)ceil_div(d.max_pages, a.CP);
+  a.ppx = (int)ceil_div(std::max(a.npairs, 1), 8);
+  a.grid = d.qkv_dtype == IDLM_F32 ? a.npairs : (int64_t)8 * a.ppx * a.maxc;
+  // ---- acceptance ----
+  AcceptPlan& c = p->acc;
+  c.R = 2 * d.N - 1;
+  c.nsub = (int)ceil_div(d.V, kSub);
+  const int64_t rows = (int64_t)std::max(d.B, 1) * c.R;
+  int S1 = (int)std::min<int64_t>(c.nsub, std::max<int64_t>(1, ceil_div(2048, rows)));
+  const int per = (int)ceil_div(c.nsub, S1);
+  c.chunk1 = per * kSub;
+  c.S1 = (int)ceil_div(d.V, c.chunk1);
+  c.spw = (int)std::min<int64_t>(c.nsub, std::max<int64_t>(1, ceil_div((int64_t)c.nsub * std::max(d.B, 1), 2048)));
+  c.S2 = (int)ceil_div(c.nsub, c.spw);
+  // ---- workspace layout ----
+  size_t o = 0;
+  p->off_status = o;
+  o = align256(o + 4);
+  p->off_attn_cnt = o;
+  o = align256(o + (size_t)a.npairs * 4);
+  // Split-K partials exist only when a context can span several chunks.
+  const size_t nparts = (a.maxc > 1 && d.qkv_dtype == IDLM_BF16) ? (size_t)a.npairs * a.maxc : 0;
+  p->off_attn_ml = o;
+  o = align256(o + nparts * a.RGp * 8);
+  p->off_attn_o = o;
+  o = align256(o + nparts * a.RGp * d.D * 4);
+  p->off_cnt1 = o;
+  o = align256(o + (size_t)d.B * 4);
+  p->off_cnt2 = o;
+  o = align256(o + (size_t)d.B * 4);
+  p->off_splan = o;
+  o = align256(o + (size_t)d.B * sizeof(SamplePlan));
+  p->off_stats = o;
+  o = align256(o + (size_t)d.B * c.R * c.S1 * 16);
+  p->off_subsum = o;
+  o = align256(o + (size_t)d.B * c.nsub * 8);
+  p->total = o;
+  return true;
+}
+
+__global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+int32_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  const size_t ntail = bytes % 16;
+  const unsigned blocks = (unsigned)std::min<size_t>(4096, std::max<size_t>(1, (n16 + 255) / 256));
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, (uint4*)ws, n16,
+                     (unsigned char*)ws + n16 * 16, ntail);
+  return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
+}
+
+}  // namespace idlm
+
+using namespace idlm;
+
+extern "C" {
+
+size_t idlm_isd_workspace_bytes(const idlm_isd_dims* d) {
+  Plan p;
+  if (!d || !make_plan(*d, &p)) return 0;
+  return p.total;
+}
+
+int32_t idlm_isd_validate(const idlm_isd_dims* d, float T) {
+  const int32_t r = check_dims(d);
+  if (r != IDLM_OK) return r;
+  return check_T(T);
+}
+
+int32_t idlm_isd_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace) return IDLM_ERR_NULL;
+  if (((uintptr_t)workspace & 255) != 0) return IDLM_ERR_WORKSPACE;
+  if (ws_bytes == 0) return IDLM_OK;
+  return launch_fill_zero(workspace, ws_bytes, (hipStream_t)stream);
+}
+
+static int32_t check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+  if (!ws) return IDLM_ERR_NULL;
+  if (((uintptr_t)ws & 255) != 0 || ws_bytes < p.total) return IDLM_ERR_WORKSPACE;
+  return IDLM_OK;
+}
+
+int32_t idlm_isd_paged_attn(const idlm_isd_dims* d, const void* q, const void* kv_pages,
+                            const int32_t* page_table, const int32_t* ctx_lens, void* attn_out,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  int32_t r = check_dims(d);
+  if (r != IDLM_OK) return r;
+  Plan p;
+  make_plan(*d, &p);
+  if ((r = check_ws(p, workspace, ws_bytes)) != IDLM_OK) return r;
+  if (d->B == 0) return IDLM_OK;
+  if (!q || !kv_pages || !page_table || !ctx_lens || !attn_out) return IDLM_ERR_NULL;
+  return launch_paged_attn(*d, p, q, kv_pages, page_table, ctx_lens, attn_out, (char*)workspace,
+                           (hipStream_t)stream);
+}
+
+int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const void* logits_mask,
+                        const int32_t* draft_tokens, uint64_t seed, float T, int32_t* out_tokens,
+                        int32_t* out_accept_len, double* out_debug, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  int32_t r = check_dims(d);
+  if (r != IDLM_OK) return r;
+  if ((r = check_T(T)) != IDLM_OK) return r;
+  Plan p;
+  make_plan(*d, &p);
+  if ((r = check_ws(p, workspace, ws_bytes)) != IDLM_OK) return r;
+  if (d->B == 0) return IDLM_OK;
+  if (!logits_clean || !out_tokens || !out_accept_len) return IDLM_ERR_NULL;
+  if (d->N > 1 && (!logits_mask || !draft_tokens)) return IDLM_ERR_NULL;
+  return launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
+                       out_accept_len, out_debug, (char*)workspace, (hipStream_t)stream);
+}
+
+int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
+                      const int32_t* page_table, const int32_t* ctx_lens,
+                      const void* logits_clean, const void* logits_mask,
+                      const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
+                      int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  int32_t r = check_dims(d);
+  if (r != IDLM_OK) return r;
+  if (N != d->N) return IDLM_ERR_DIMS;
+  if ((r = check_T(T)) != IDLM_OK) return r;
+  Plan p;
+  make_plan(*d, &p);
+  if ((r = check_ws(p, workspace, ws_bytes)) != IDLM_OK) return r;
+  if (d->B == 0) return IDLM_OK;
+  if (!q || !kv_pages || !page_table || !ctx_lens || !attn_out) return IDLM_ERR_NULL;
+  if (!logits_clean || !out_tokens || !out_accept_len) return IDLM_ERR_NULL;
+  if (d->N > 1 && (!logits_mask || !draft_tokens)) return IDLM_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  r = launch_paged_attn(*d, p, q, kv_pages, page_table, ctx_lens, attn_out, (char*)workspace, s);
+  if (r != IDLM_OK) return r;
+  return launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
+                       out_accept_len, nullptr, (char*)workspace, s);
+}
+
+int32_t idlm_isd_read_status(const void* workspace, void* stream, int32_t* host_code) {
+  if (!workspace || !host_code) return IDLM_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipStreamSynchronize(s) != hipSuccess) return IDLM_ERR_HIP;
+  int32_t word = 0;
+  if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    return IDLM_ERR_HIP;
+  *host_code = word ? IDLM_ERR_DEVICE_DATA : IDLM_OK;
+  return IDLM_OK;
+}
+
+const char* idlm_isd_strerror(int32_t status) {
+  switch (status) {
+    case IDLM_OK: return "ok";
+    case IDLM_ERR_NULL: return "a required pointer is NULL";
+    case IDLM_ERR_DIMS: return "sizes out of range or inconsistent";
+    case IDLM_ERR_UNSUPPORTED: return "sizes valid but not supported (D, page size or tile rows)";
+    case IDLM_ERR_TEMPERATURE: return "temperature must be finite and >= 0";
+    case IDLM_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case IDLM_ERR_HIP: return "HIP runtime error";
+    case IDLM_ERR_DEVICE_DATA: return "kernels saw invalid device data (page id, context or draft)";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

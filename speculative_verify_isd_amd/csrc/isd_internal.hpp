@@ -1,0 +1,73 @@
+// Internal declarations shared by the library's translation units: the
+// workspace plan and the kernel launchers.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/idlm_isd.h"
+
+namespace idlm {
+
+constexpr int kPage = 16;
+constexpr int kSub = 2048;  // acceptance sub-chunk: 256 threads x 8 elements
+
+// Sticky device status bits (workspace word 0).
+enum : int32_t { kBadPage = 1, kBadCtx = 2, kBadDraft = 4 };
+
+// How one attention launch is cut into work-groups.
+struct AttnPlan {
+  int R, G, RG;   // step rows, heads per KV head, query rows per (b, kv head)
+  int WR;         // waves sharing a page set, one per 32 query rows (1, 2 or 4)
+  int RGp;        // RG padded to 32 * WR
+  int CP;         // pages per context chunk (split-K unit), multiple of 8
+  int maxc;       // chunks of the longest possible context
+  int npairs;     // B * Hkv
+  int ppx;        // (b, kv head) pairs per XCD slot: ceil(npairs / 8)
+  int64_t grid;   // work-groups launched
+};
+
+// How one acceptance launch is cut.
+struct AcceptPlan {
+  int R;          // rows per sequence: N clean + K mask
+  int nsub;       // kSub-element sub-chunks per row
+  int S1;         // stats work-groups per row
+  int chunk1;     // elements per stats work-group (multiple of kSub)
+  int spw;        // sub-chunks per sampling work-group
+  int S2;         // sampling work-groups per sequence
+};
+
+// Per-sequence hand-over from the ratio test to the sampler.
+struct SamplePlan {
+  int32_t mode;    // 0 residual max(0, p_j - q_j), 1 p row only (bonus / fallback), 2 done
+  int32_t row_p;   // clean row holding p
+  int32_t row_q;   // mask row holding q (residual mode)
+  int32_t j;       // output index of the sampled token
+  double mp, sp;   // raw-logit max and sum of exp2((l - m) * log2e / T) of row_p
+  double mq, sq;   // same for row_q
+  double u2;       // sampling uniform
+  double pad;
+};
+
+struct Plan {
+  AttnPlan attn;
+  AcceptPlan acc;
+  size_t off_status, off_attn_cnt, off_attn_ml, off_attn_o;
+  size_t off_cnt1, off_cnt2, off_splan, off_stats, off_subsum;
+  size_t total;
+};
+
+bool make_plan(const idlm_isd_dims& d, Plan* p);
+
+int32_t launch_paged_attn(const idlm_isd_dims& d, const Plan& p, const void* q, const void* kv,
+                          const int32_t* page_table, const int32_t* ctx_lens, void* out,
+                          char* ws, hipStream_t s);
+
+int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
+                      const int32_t* drafts, uint64_t seed, float T, int32_t* out_tokens,
+                      int32_t* out_len, double* out_debug, char* ws, hipStream_t s);
+
+int32_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
+
+}  // namespace idlm

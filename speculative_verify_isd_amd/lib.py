@@ -1,0 +1,269 @@
+"""ctypes binding of libidlm_isd.so (C ABI in include/idlm_isd.h).
+
+Argument marshalling only: every function here checks tensor dtypes, devices
+and contiguity, then passes raw device pointers and torch's current HIP
+stream to the entry point of the same name.  No step arithmetic happens in
+Python and there is no fallback: if the library is missing, ``load()``
+raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libidlm_isd.so")
+
+IDLM_BF16 = 0
+IDLM_F32 = 1
+
+STATUS = {
+    0: "IDLM_OK",
+    1: "IDLM_ERR_NULL",
+    2: "IDLM_ERR_DIMS",
+    3: "IDLM_ERR_UNSUPPORTED",
+    4: "IDLM_ERR_TEMPERATURE",
+    5: "IDLM_ERR_WORKSPACE",
+    6: "IDLM_ERR_HIP",
+    7: "IDLM_ERR_DEVICE_DATA",
+}
+
+# Every entry point declared in include/idlm_isd.h.
+ENTRY_POINTS = (
+    "idlm_isd_workspace_bytes",
+    "idlm_isd_validate",
+    "idlm_isd_workspace_init",
+    "idlm_isd_paged_attn",
+    "idlm_isd_accept",
+    "idlm_isd_step",
+    "idlm_isd_read_status",
+    "idlm_isd_strerror",
+)
+
+
+class IdlmError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = int(code)
+        super().__init__(f"{where}: {STATUS.get(self.code, self.code)} ({strerror(self.code)})")
+
+
+class Dims(ctypes.Structure):
+    """idlm_isd_dims."""
+
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "B", "N", "Hq", "Hkv", "D", "V", "page_size", "max_pages", "num_pages",
+        "qkv_dtype", "logits_dtype")]
+
+
+def make_dims(B, N, Hq, Hkv, D, V, max_pages, num_pages, qkv_dtype="bf16", logits_dtype="bf16",
+              page_size=16):
+    code = {"bf16": IDLM_BF16, "f32": IDLM_F32}
+    return Dims(B, N, Hq, Hkv, D, V, page_size, max_pages, num_pages, code[qkv_dtype],
+                code[logits_dtype])
+
+
+_lib = None
+
+
+def load():
+    """Load libidlm_isd.so (once); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m speculative_verify_isd_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(Dims)
+    i32, u64, f32, sz = ctypes.c_int32, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "idlm_isd_workspace_bytes": (sz, [D]),
+        "idlm_isd_validate": (i32, [D, f32]),
+        "idlm_isd_workspace_init": (i32, [P, sz, P]),
+        "idlm_isd_paged_attn": (i32, [D, P, P, P, P, P, P, sz, P]),
+        "idlm_isd_accept": (i32, [D, P, P, P, u64, f32, P, P, P, P, sz, P]),
+        "idlm_isd_step": (i32, [D, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, sz, P]),
+        "idlm_isd_read_status": (i32, [P, P, ctypes.POINTER(i32)]),
+        "idlm_isd_strerror": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def strerror(code):
+    return load().idlm_isd_strerror(int(code)).decode()
+
+
+def _check(code, where):
+    if code != 0:
+        raise IdlmError(code, where)
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, dtypes, name, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA/HIP tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _fdt(dims_code):
+    torch = _torch()
+    return (torch.bfloat16,) if dims_code == IDLM_BF16 else (torch.float32,)
+
+
+def _i32():
+    return (_torch().int32,)
+
+
+def idlm_isd_workspace_bytes(dims):
+    return int(load().idlm_isd_workspace_bytes(ctypes.byref(dims)))
+
+
+def idlm_isd_validate(dims, T):
+    return int(load().idlm_isd_validate(ctypes.byref(dims), float(T)))
+
+
+def alloc_workspace(dims, device="cuda"):
+    """Allocate (256-byte aligned) and initialise a workspace for ``dims``."""
+    torch = _torch()
+    n = idlm_isd_workspace_bytes(dims)
+    if n == 0:
+        raise IdlmError(2, "idlm_isd_workspace_bytes")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    idlm_isd_workspace_init(ws)
+    return ws
+
+
+def idlm_isd_workspace_init(ws):
+    _check(load().idlm_isd_workspace_init(_ptr(ws, (_torch().uint8,), "workspace"),
+                                          ws.numel(), _stream()), "idlm_isd_workspace_init")
+
+
+def idlm_isd_paged_attn(dims, q, kv_pages, page_table, ctx_lens, attn_out, ws):
+    ft = _fdt(dims.qkv_dtype)
+    _check(load().idlm_isd_paged_attn(
+        ctypes.byref(dims), _ptr(q, ft, "q"), _ptr(kv_pages, ft, "kv_pages"),
+        _ptr(page_table, _i32(), "page_table"), _ptr(ctx_lens, _i32(), "ctx_lens"),
+        _ptr(attn_out, ft, "attn_out"), _ptr(ws, (_torch().uint8,), "workspace"), ws.numel(),
+        _stream()), "idlm_isd_paged_attn")
+
+
+def idlm_isd_accept(dims, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
+                    out_accept_len, out_debug, ws):
+    ft = _fdt(dims.logits_dtype)
+    torch = _torch()
+    _check(load().idlm_isd_accept(
+        ctypes.byref(dims), _ptr(logits_clean, ft, "logits_clean"),
+        _ptr(logits_mask, ft, "logits_mask", allow_none=True),
+        _ptr(draft_tokens, _i32(), "draft_tokens", allow_none=True),
+        ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), float(T),
+        _ptr(out_tokens, _i32(), "out_tokens"), _ptr(out_accept_len, _i32(), "out_accept_len"),
+        _ptr(out_debug, (torch.float64,), "out_debug", allow_none=True),
+        _ptr(ws, (torch.uint8,), "workspace"), ws.numel(), _stream()), "idlm_isd_accept")
+
+
+def idlm_isd_step(dims, q, kv_pages, page_table, ctx_lens, logits_clean, logits_mask,
+                  draft_tokens, seed, N, T, out_tokens, out_accept_len, attn_out, ws):
+    fq = _fdt(dims.qkv_dtype)
+    fl = _fdt(dims.logits_dtype)
+    torch = _torch()
+    _check(load().idlm_isd_step(
+        ctypes.byref(dims), _ptr(q, fq, "q"), _ptr(kv_pages, fq, "kv_pages"),
+        _ptr(page_table, _i32(), "page_table"), _ptr(ctx_lens, _i32(), "ctx_lens"),
+        _ptr(logits_clean, fl, "logits_clean"),
+        _ptr(logits_mask, fl, "logits_mask", allow_none=True),
+        _ptr(draft_tokens, _i32(), "draft_tokens", allow_none=True),
+        ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), int(N), float(T),
+        _ptr(out_tokens, _i32(), "out_tokens"), _ptr(out_accept_len, _i32(), "out_accept_len"),
+        _ptr(attn_out, fq, "attn_out"), _ptr(ws, (torch.uint8,), "workspace"), ws.numel(),
+        _stream()), "idlm_isd_step")
+
+
+def idlm_isd_read_status(ws):
+    code = ctypes.c_int32(-1)
+    _check(load().idlm_isd_read_status(_ptr(ws, (_torch().uint8,), "workspace"), _stream(),
+                                       ctypes.byref(code)), "idlm_isd_read_status")
+    return int(code.value)
+
+
+# ---------------------------------------------------------------------------
+# Workload upload (storage arrays -> device tensors of the boundary formats)
+# ---------------------------------------------------------------------------
+def _to_dev(a, dtype, device):
+    torch = _torch()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+class DeviceStep:
+    """Device tensors and workspace for one workload, plus the step's calls."""
+
+    def __init__(self, w, device="cuda"):
+        torch = _torch()
+        self.w = w
+        self.dims = make_dims(w.B, w.N, w.Hq, w.Hkv, w.D, w.V, w.max_pages, max(1, w.num_pages),
+                              w.qkv_dtype, w.logits_dtype)
+        self.q = _to_dev(w.q, w.qkv_dtype, device)
+        self.kv = _to_dev(w.kv_pages, w.qkv_dtype, device)
+        self.page_table = torch.from_numpy(np.ascontiguousarray(w.page_table)).to(device)
+        self.ctx_lens = torch.from_numpy(np.ascontiguousarray(w.ctx_lens)).to(device)
+        self.lc = _to_dev(w.logits_clean, w.logits_dtype, device)
+        self.lm = _to_dev(w.logits_mask, w.logits_dtype, device) if w.N > 1 else None
+        self.drafts = torch.from_numpy(np.ascontiguousarray(w.draft_tokens)).to(device) \
+            if w.N > 1 else None
+        qdt = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
+        self.out = torch.zeros(self.q.shape, dtype=qdt, device=device)
+        self.tokens = torch.full((w.B, w.N), -7, dtype=torch.int32, device=device)
+        self.lens = torch.zeros(w.B, dtype=torch.int32, device=device)
+        self.debug = torch.zeros((w.B, w.N + 1, 4), dtype=torch.float64, device=device)
+        self.ws = alloc_workspace(self.dims, device)
+
+    def attn(self):
+        idlm_isd_paged_attn(self.dims, self.q, self.kv, self.page_table, self.ctx_lens, self.out,
+                            self.ws)
+
+    def accept(self, seed=None, T=None, debug=True):
+        idlm_isd_accept(self.dims, self.lc, self.lm, self.drafts,
+                        self.w.seed if seed is None else seed, self.w.T if T is None else T,
+                        self.tokens, self.lens, self.debug if debug else None, self.ws)
+
+    def step(self, seed=None, T=None):
+        idlm_isd_step(self.dims, self.q, self.kv, self.page_table, self.ctx_lens, self.lc, self.lm,
+                      self.drafts, self.w.seed if seed is None else seed, self.w.N,
+                      self.w.T if T is None else T, self.tokens, self.lens, self.out, self.ws)
+
+    def out_f64(self):
+        return self.out.to(_torch().float64).cpu().numpy()

@@ -33,6 +33,8 @@ c64n8  B=64, N=8, 64/8 heads, D=128, bfloat16, ctx ~ U[4096, 32768],
        sigma = 0.5, T=0.7.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -49,14 +51,30 @@ def f32_to_bf16_bits(x):
 
 
 def _normal_store(rng, shape, scale, dtype, block=1 << 24):
-    """N(0, scale^2) draws in storage dtype, generated in blocks to bound memory."""
+    """N(0, scale^2) draws in storage dtype.
+
+    Large draws are cut into fixed blocks, each with its own PCG64 stream
+    spawned from one seed taken from ``rng``; blocks fill in parallel threads
+    (numpy releases the GIL), so the result depends only on the seed.
+    """
     n = int(np.prod(shape))
-    if dtype == "f32":
-        return (rng.standard_normal(n, dtype=np.float32) * np.float32(scale)).reshape(shape)
-    out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, block):
-        e = min(n, s + block)
-        out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32) * np.float32(scale))
+    base = int(rng.integers(0, 2 ** 63))
+    nblk = max(1, (n + block - 1) // block)
+    seqs = np.random.SeedSequence(base).spawn(nblk)
+    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+
+    def fill(i):
+        s, e = i * block, min(n, (i + 1) * block)
+        g = np.random.Generator(np.random.PCG64(seqs[i]))
+        x = g.standard_normal(e - s, dtype=np.float32)
+        x *= np.float32(scale)
+        out[s:e] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    if nblk == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(nblk)))
     return out.reshape(shape)
 
 

@@ -1,0 +1,122 @@
+"""The C ABI on the host: the library loads, exports every entry point that
+include/idlm_isd.h declares, and validates sizes, temperature, pointers and
+workspace before touching the GPU.  No kernel is launched here."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from speculative_verify_isd_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idlm_isd.h")
+
+
+@pytest.fixture(scope="module")
+def so():
+    if not os.path.exists(L.LIB_PATH):
+        from speculative_verify_isd_amd.build import build
+        build()
+    return L.load()
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(idlm_isd_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_entry_points() == sorted(L.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(so):
+    for name in declared_entry_points():
+        assert hasattr(so, name), name
+
+
+def good(**kw):
+    base = dict(B=64, N=4, Hq=32, Hkv=8, D=128, V=151936, max_pages=1024, num_pages=40000)
+    base.update(kw)
+    return L.make_dims(**base)
+
+
+def test_validate_accepts_the_step_shapes(so):
+    for d in (good(), good(N=8, Hq=64), good(B=1, D=64, Hq=8, Hkv=2, V=512, qkv_dtype="f32",
+                                              logits_dtype="f32"), good(N=1), good(B=0)):
+        assert L.idlm_isd_validate(d, 1.0) == 0
+    assert L.idlm_isd_validate(good(), 0.0) == 0  # greedy
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), 2), (dict(N=17), 2), (dict(Hq=30), 2), (dict(Hkv=0), 2), (dict(V=0), 2),
+    (dict(B=-1), 2), (dict(max_pages=0), 2), (dict(num_pages=0), 2),
+    (dict(D=96), 3), (dict(page_size=8), 3), (dict(N=9, Hq=64), 3),
+])
+def test_validate_rejects(so, kw, code):
+    assert L.idlm_isd_validate(good(**kw), 1.0) == code
+    assert L.idlm_isd_workspace_bytes(good(**kw)) == 0
+
+
+def test_validate_rejects_bad_dtype(so):
+    d = good()
+    d.qkv_dtype = 5
+    assert L.idlm_isd_validate(d, 1.0) == 2
+
+
+@pytest.mark.parametrize("T", [-0.1, math.nan, math.inf])
+def test_validate_rejects_temperature(so, T):
+    assert L.idlm_isd_validate(good(), T) == 4
+
+
+def test_null_dims(so):
+    assert so.idlm_isd_validate(None, 1.0) == 1
+    assert so.idlm_isd_workspace_bytes(None) == 0
+
+
+def test_workspace_bytes_grow_with_batch(so):
+    a = L.idlm_isd_workspace_bytes(good(B=16))
+    b = L.idlm_isd_workspace_bytes(good(B=64))
+    assert 0 < a < b
+    assert b % 256 == 0
+
+
+def test_entry_points_validate_before_launch(so):
+    # All of these return before any HIP call: bad sizes, NULL or short workspace.
+    d = good()
+    n = L.idlm_isd_workspace_bytes(d)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert so.idlm_isd_paged_attn(ctypes.byref(good(D=96)), fake, fake, fake, fake, fake,
+                                  fake, n, None) == 3
+    assert so.idlm_isd_paged_attn(ctypes.byref(d), fake, fake, fake, fake, fake, None, n,
+                                  None) == 1
+    assert so.idlm_isd_paged_attn(ctypes.byref(d), fake, fake, fake, fake, fake, fake, n - 256,
+                                  None) == 5
+    misaligned = ctypes.c_void_p((1 << 20) + 8)
+    assert so.idlm_isd_accept(ctypes.byref(d), fake, fake, fake, 1, 1.0, fake, fake, None,
+                              misaligned, n, None) == 5
+    assert so.idlm_isd_accept(ctypes.byref(d), fake, fake, fake, 1, -1.0, fake, fake, None,
+                              fake, n, None) == 4
+    assert so.idlm_isd_accept(ctypes.byref(d), None, fake, fake, 1, 1.0, fake, fake, None,
+                              fake, n, None) == 1
+    assert so.idlm_isd_step(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, 1, 3, 1.0,
+                            fake, fake, fake, fake, n, None) == 2  # N repeated must match
+    assert so.idlm_isd_read_status(None, None, None) == 1
+    assert so.idlm_isd_workspace_init(misaligned, 1024, None) == 5
+
+
+def test_empty_batch_is_a_no_op(so):
+    d = good(B=0)
+    n = L.idlm_isd_workspace_bytes(d)
+    fake = ctypes.c_void_p(1 << 20)
+    assert so.idlm_isd_step(ctypes.byref(d), None, None, None, None, None, None, None, 1, 4, 1.0,
+                            None, None, None, fake, n, None) == 0
+
+
+def test_strerror(so):
+    for code, name in L.STATUS.items():
+        s = L.strerror(code)
+        assert isinstance(s, str) and s
+    assert L.strerror(99) == "unknown status"
