@@ -54,6 +54,24 @@ def accept_bytes(w, lens, kp):
     return (rows + 2 * resid + bonus) * w.V * es + w.B * (w.N + 1) * 4
 
 
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain 1 GiB copy), or None
+    when the kernel sources changed after those counters were taken."""
+    import hashlib
+
+    tfile = os.path.join(ROOT, "profiles", "isd_paged_attn_c64_traffic.json")
+    if not os.path.exists(tfile):
+        return None
+    t = json.load(open(tfile))
+    csrc = os.path.join(ROOT, "speculative_verify_isd_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                   for f in ("isd_attn.hip", "isd_accept.hip"))
+    if hashlib.sha256(src).hexdigest()[:16] != t.get("kernel_source_sha256_16"):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
 def cpu_baseline(w, n_seq):
     """Time the oracle on the first ``n_seq`` sequences and scale to the batch."""
     from oracle.accept import isd_accept
@@ -149,13 +167,7 @@ def main():
     attn_gbs = a_bytes / (attn_ms * 1e-3) / 1e9
     acc_gbs = c_bytes / (acc_ms * 1e-3) / 1e9
 
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "isd_paged_attn_c64_traffic.json")
-    if os.path.exists(tfile):
-        try:
-            traffic = json.load(open(tfile)).get("hbm_bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic()
 
     res = {
         "metric": "ISD steps/s + accepted tok/s at C=64, N=4; % of HBM roofline (rocprof)",
