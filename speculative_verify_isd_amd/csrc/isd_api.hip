@@ -35,12 +35,6 @@ int32_t check_T(float T) {
   return IDLM_OK;
 }
 
-int pow2_floor(int64_t x) {
-  int p = 1;
-  while ((int64_t)p * 2 <= x) p *= 2;
-  return p;
-}
-
 }  // namespace
 
 bool make_plan(const idlm_isd_dims& d, Plan* p) {
@@ -54,15 +48,7 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   a.WR = a.RG <= 32 ? 1 : (a.RG <= 64 ? 2 : 4);
   a.RGp = 32 * a.WR;
   a.npairs = d.B * d.Hkv;
-  // Chunk so that a full batch gives ~2048 work-groups, within [8, cap] pages;
-  // larger query tiles get longer chunks so their fp32 partials stay a few
-  // percent of the KV bytes they summarise.
-  const int cap = a.WR == 1 ? 64 : 256;
-  const int64_t want = ((int64_t)a.npairs * d.max_pages) / 2048;
-  a.CP = (int)std::min<int64_t>(cap, std::max<int64_t>(8, pow2_floor(std::max<int64_t>(want, 1))));
-  a.maxc = (int)ceil_div(d.max_pages, a.CP);
-  a.ppx = (int)ceil_div(std::max(a.npairs, 1), 8);
-  a.grid = d.qkv_dtype == IDLM_F32 ? a.npairs : (int64_t)8 * a.ppx * a.maxc;
+  a.max_lanes = kMaxWaves / a.WR;
   // ---- acceptance ----
   AcceptPlan& c = p->acc;
   c.R = 2 * d.N - 1;
@@ -79,13 +65,12 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   p->off_status = o;
   o = align256(o + 4);
   p->off_attn_cnt = o;
-  o = align256(o + (size_t)a.npairs * 4);
-  // Split-K partials exist only when a context can span several chunks.
-  const size_t nparts = (a.maxc > 1 && d.qkv_dtype == IDLM_BF16) ? (size_t)a.npairs * a.maxc : 0;
+  // Streaming attention: two partial-state slots per wave-lane (bf16 path).
+  const size_t nslots = d.qkv_dtype == IDLM_BF16 ? (size_t)a.max_lanes * 2 : 0;
   p->off_attn_ml = o;
-  o = align256(o + nparts * a.RGp * 8);
+  o = align256(o + nslots * a.RGp * 8);
   p->off_attn_o = o;
-  o = align256(o + nparts * a.RGp * d.D * 4);
+  o = align256(o + nslots * a.RGp * d.D * 4);
   p->off_cnt1 = o;
   o = align256(o + (size_t)d.B * 4);
   p->off_cnt2 = o;

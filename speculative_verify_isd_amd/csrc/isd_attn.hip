@@ -9,33 +9,35 @@
 // as they approach compute-bound?"); the paged cache is from "Serving
 // (SGLang)".
 //
-// Work decomposition
-//   One work-group (4 waves of 64) owns one context chunk of CP pages of one
-//   (b, kv head) pair.  All R*G query rows of the pair share every K/V page,
-//   so the page is read once and reused across the whole query tile: the
-//   tile rows are the MFMA "N" side, 16 per block.  Each wave carries 32
-//   query rows (two 16-row blocks); WR = ceil(R*G/32) waves split the rows
-//   and the other 4/WR wave lanes split the chunk's pages two at a time.
+// Work decomposition (bf16 path)
+//   The batch's KV is a list of units, one per (sequence b, KV head h, page),
+//   in (b, h, page) order.  A persistent grid of wave-lanes splits that list
+//   into equal contiguous runs, so every lane streams the same number of
+//   pages whatever the context mix.  A run crosses (b, h) pairs: each piece
+//   of a pair is a segment.  A segment that covers its whole pair writes the
+//   final output; a partial one writes its softmax state (m, l, O) to one of
+//   the lane's two slots (a partial segment can only be a lane's first or
+//   last), and attn_merge_kernel combines the pieces in unit order.
+//
+//   All R*G query rows of a pair share every K/V page, so each page is read
+//   once and reused across the query tile: a wave carries 32 query rows (two
+//   16-row MFMA blocks, rows r*G + g on the MFMA N side).  For R*G > 32,
+//   WR = 2 or 4 waves of a work-group walk the same run, one 32-row group
+//   each; otherwise the 4 waves are 4 independent lanes.
 //
 //   Per two pages (32 tokens) and 16-row block a wave runs
 //     S^T[tok][row] = K[tok][:] . Q[row][:]   (D/32 x mfma_f32_16x16x32_bf16)
-//     online softmax on S^T (rows live in lanes, tokens in registers)
+//     online softmax on S^T (rows in lanes, tokens in registers)
 //     O^T[d][row]  += V^T[d][tok] . P^T[tok][row]  (D/16 x 16x16x32)
 //   The S^T accumulator layout is exactly the B-operand layout P^T needs,
-//   and O^T keeps rows in lanes, so the softmax rescale needs no shuffles.
+//   and O^T keeps rows in lanes, so the softmax needs no data movement
+//   beyond two row-swap permutes for the max.
 //
-//   The page layout is chosen for these operands: every K fragment load is
-//   one contiguous 1 KiB per wave (16 B per lane) and every V^T fragment load
-//   one contiguous 512 B, so the stream is fully coalesced straight into
-//   VGPRs with no LDS round trip.  LDS is used only to merge the waves'
-//   partial softmax states at the end of the chunk.
-//
-//   Split-K across work-groups: a chunk writes (m, l, O) partials; the last
-//   work-group of a pair to finish (atomic counter) merges them in fixed
-//   chunk order, so results do not depend on scheduling.  Work-groups are
-//   laid out so that all chunks of a pair land on the same XCD (dispatch is
-//   round-robin over the 8 XCDs), which keeps the merge reads in that XCD's
-//   L2.
+//   The page layout is chosen for these operands: each K fragment load is a
+//   contiguous 1 KiB per wave (16 B per lane) and each V^T fragment load a
+//   contiguous 512 B, so pages stream straight into VGPRs.  Two register
+//   buffers keep one step's loads in flight while the previous step
+//   computes; page ids are wave-uniform loads.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -45,7 +47,6 @@ namespace idlm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 
@@ -55,15 +56,13 @@ struct AttnArgs {
   const int32_t* page_table;
   const int32_t* ctx_lens;
   void* out;
-  float* part_o;
-  float2* part_ml;
-  unsigned* counters;
+  float* part_o;    // [nlanes][2][ROWS][D]
+  float2* part_ml;  // [nlanes][2][ROWS]
   int32_t* status;
-  int B, R, Hq, Hkv, G, RG, max_pages, num_pages, CP, maxc, npairs, ppx;
+  int B, R, Hq, Hkv, G, RG, D, max_pages, num_pages;
+  int nlanes;       // wave-lanes of the streaming grid
   float scale_log2;  // log2(e) / sqrt(D)
 };
-
-__device__ inline float bf16_to_f32(u16 v) { return __uint_as_float(((unsigned)v) << 16); }
 
 __device__ inline u16 f32_to_bf16_rne(float f) {
   unsigned u = __float_as_uint(f);
@@ -73,241 +72,429 @@ __device__ inline u16 f32_to_bf16_rne(float f) {
 
 __device__ inline void flag(int32_t* status, int32_t bit) { atomicOr(status, bit); }
 
-// Map a work-group index to (pair, chunk) so every chunk of a pair shares an
-// XCD: dispatch sends work-group i to XCD i % 8.
-__device__ inline void decode_wg(int64_t wg, int ppx, int* pair, int* chunk) {
-  const int x = (int)(wg & 7);
-  const int64_t k = wg >> 3;
-  *pair = x + 8 * (int)(k % ppx);
-  *chunk = (int)(k / ppx);
-}
-
-// Validated context length of sequence b (clamped, flagged).
-__device__ inline int load_ctx(const AttnArgs& a, int b) {
-  int ctx = a.ctx_lens[b];
+// Context length clamped to [R, 16*max_pages]; `report` sets the status bit
+// when it had to clamp.
+__device__ inline int clamp_ctx(const AttnArgs& a, int ctx, bool report) {
   const int hi = kPage * a.max_pages;
   if (ctx < a.R || ctx > hi) {
-    if (threadIdx.x == 0) flag(a.status, kBadCtx);
+    if (report) flag(a.status, kBadCtx);
     ctx = ctx < a.R ? a.R : hi;
   }
   return ctx;
 }
 
-__device__ inline int load_page(const AttnArgs& a, int b, int p) {
-  int phys = a.page_table[(size_t)b * a.max_pages + p];
-  if ((unsigned)phys >= (unsigned)a.num_pages) {
-    flag(a.status, kBadPage);
-    phys = 0;
+__device__ inline int pages_of(int ctx) { return (ctx + kPage - 1) / kPage; }
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA building blocks
+// ---------------------------------------------------------------------------
+
+// K and V^T fragments of two consecutive pages for one wave.
+template <int D>
+struct KVFrag {
+  bf16x8 k[2][D / 32];
+  bf16x8 v[D / 16];  // page a's 4 tokens, then page b's 4 tokens
+};
+
+// Issue the loads of one two-page step.  K: one contiguous 1 KiB per 32-wide
+// d step (16 B per lane); V^T: one contiguous 512 B per 16-wide d block.
+template <int D>
+__device__ inline void load_step(KVFrag<D>& f, const u16* kva, const u16* kvb, size_t v_off,
+                                 int lane) {
+  constexpr int NC = D / 32, ND = D / 16;
+  const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    f.k[0][c] = __builtin_bit_cast(bf16x8, *(const uint4*)(kva + 512 * c + 8 * lane));
+    f.k[1][c] = __builtin_bit_cast(bf16x8, *(const uint4*)(kvb + 512 * c + 8 * lane));
   }
-  return phys;
+#pragma unroll
+  for (int j = 0; j < ND; ++j) {
+    const size_t o = v_off + (size_t)(16 * j + col) * kPage + 4 * grp;
+    const uint2 va = *(const uint2*)(kva + o);
+    const uint2 vb = *(const uint2*)(kvb + o);
+    f.v[j] = __builtin_bit_cast(bf16x8, make_uint4(va.x, va.y, vb.x, vb.y));
+  }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 MFMA path
-// ---------------------------------------------------------------------------
-template <int D, int WR>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NC = D / 32;  // K-dim steps of the QK product
-  constexpr int ND = D / 16;  // 16-wide d blocks of the PV product
-  constexpr int WK = 4 / WR;  // waves walking the pages
-  constexpr int ROWS = 32 * WR;
+// Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap permutes (no LDS round trip).
+__device__ inline float max_over_rows(float v) {
+  const unsigned b = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const unsigned c = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
 
-  __shared__ float lds_o[4][32][D];
-  __shared__ float lds_ml[4][32][2];
-  __shared__ int lds_last;
+// Online-softmax rescaling is lazy: the running max (log2 units) is raised
+// only when a new score exceeds it by more than kLazyTau, so between raises
+// the weights stay below 2^kLazyTau and the accumulators are not touched.
+// The final normalisation uses the same running max, so this is exact.
+constexpr float kLazyTau = 8.0f;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int rgrp = wave % WR, pw = wave / WR;
-  const int col = lane & 15, grp = lane >> 4;
-
-  int pair, chunk;
-  decode_wg(blockIdx.x, a.ppx, &pair, &chunk);
-  if (pair >= a.npairs) return;
-  const int b = pair / a.Hkv, kvh = pair % a.Hkv;
-  const int ctx = load_ctx(a, b);
-  const int npages = (ctx + kPage - 1) / kPage;
-  const int nch = (npages + a.CP - 1) / a.CP;
-  if (chunk >= nch) return;
-  const int pbeg = chunk * a.CP;
-  const int pend = min(npages, pbeg + a.CP);
-
-  const u16* qb = (const u16*)a.q;
-  const u16* kvb = (const u16*)a.kv;
-
-  // Query fragments (B operand of S^T = K Q^T): row = lane's column, eight
-  // consecutive d per lane; k-step c covers d chunk 4c + grp.
-  bf16x8 qf[2][NC];
-  int pos[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int i = rgrp * 32 + rb * 16 + col;
-    const bool valid = i < a.RG;
-    const int r = valid ? i / a.G : a.R - 1;
-    const int g = valid ? i % a.G : 0;
-    pos[rb] = ctx - a.R + r;
-    const u16* qp = qb + (((size_t)b * a.R + r) * a.Hq + (size_t)kvh * a.G + g) * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint4 v = valid ? *(const uint4*)(qp + 8 * (4 * c + grp)) : make_uint4(0, 0, 0, 0);
-      qf[rb][c] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
-  f32x4 acc[2][ND];
+// One two-page step for this wave's two 16-row blocks: S^T = K Q^T, online
+// softmax in exp2 space, O^T += V^T P^T.  MASKED applies the causal mask and
+// a missing second page; most steps are fully visible and skip it.
+template <int D, bool MASKED>
+__device__ inline void compute_step(const KVFrag<D>& f, const bf16x8 (&qf)[2][D / 32],
+                                    const int (&pos)[2], int ta, bool hasa, bool hasb,
+                                    float c2, float (&m)[2], float (&l)[2],
+                                    f32x4 (&acc)[2][D / 16]) {
+  constexpr int NC = D / 32, ND = D / 16;
+  f32x4 sc[2][2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int j = 0; j < ND; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const size_t page_elems = (size_t)2 * a.Hkv * kPage * D;
-  const size_t head_off = (size_t)kvh * kPage * D;
-  const size_t v_off = (size_t)a.Hkv * kPage * D;
-
-  for (int p0 = pbeg + 2 * pw; p0 < pend; p0 += 2 * WK) {
-    const bool hasb = p0 + 1 < pend;
-    const int phys_a = load_page(a, b, p0);
-    const int phys_b = hasb ? load_page(a, b, p0 + 1) : phys_a;
-    const u16* Ka = kvb + (size_t)phys_a * page_elems + head_off;
-    const u16* Kb = kvb + (size_t)phys_b * page_elems + head_off;
-
-    bf16x8 ka[NC], kb[NC];
+    for (int pg = 0; pg < 2; ++pg) sc[rb][pg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      ka[c] = __builtin_bit_cast(bf16x8, *(const uint4*)(Ka + 512 * c + 8 * lane));
-      kb[c] = __builtin_bit_cast(bf16x8, *(const uint4*)(Kb + 512 * c + 8 * lane));
-    }
-    bf16x4 va[ND], vb[ND];
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int j = 0; j < ND; ++j) {
-      const size_t o = v_off + (size_t)(16 * j + col) * kPage + 4 * grp;
-      va[j] = __builtin_bit_cast(bf16x4, *(const uint2*)(Ka + o));
-      vb[j] = __builtin_bit_cast(bf16x4, *(const uint2*)(Kb + o));
-    }
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg)
+        sc[rb][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[pg][c], qf[rb][c], sc[rb][pg], 0, 0, 0);
 
-    const int ta = p0 * kPage + 4 * grp;  // first token of this lane in page a
-    const int tb = ta + kPage;
+  float mx[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    if (MASKED) {
+      const int tb = ta + kPage;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[rb][0][e] = (hasa && ta + e <= pos[rb]) ? sc[rb][0][e] : -INFINITY;
+        sc[rb][1][e] = (hasb && tb + e <= pos[rb]) ? sc[rb][1][e] : -INFINITY;
+      }
+    }
+    float v = fmaxf(fmaxf(sc[rb][0][0], sc[rb][0][1]), fmaxf(sc[rb][0][2], sc[rb][0][3]));
+    v = fmaxf(v, fmaxf(fmaxf(sc[rb][1][0], sc[rb][1][1]), fmaxf(sc[rb][1][2], sc[rb][1][3])));
+    mx[rb] = max_over_rows(v) * c2;
+  }
+  if (__any((mx[0] > m[0] + kLazyTau) || (mx[1] > m[1] + kLazyTau))) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qf[rb][c], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[c], qf[rb][c], sb, 0, 0, 0);
-      }
-      float xa[4], xb[4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xa[e] = (ta + e <= pos[rb]) ? sa[e] * a.scale_log2 : -INFINITY;
-        xb[e] = (hasb && tb + e <= pos[rb]) ? sb[e] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, fmaxf(xa[e], xb[e]));
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[rb], mx);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2f(m[rb] - muse);
+      const float mnew = fmaxf(m[rb], mx[rb]);
+      const float alpha = __builtin_amdgcn_exp2f(m[rb] - (mnew == -INFINITY ? 0.f : mnew));
       m[rb] = mnew;
-      float ps = 0.f;
-      bf16x8 pf;
+      l[rb] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pa = exp2f(xa[e] - muse);
-        const float pb = exp2f(xb[e] - muse);
-        ps += pa + pb;
-        pf[e] = (__bf16)pa;
-        pf[4 + e] = (__bf16)pb;
-      }
-      l[rb] = l[rb] * alpha + ps;
-#pragma unroll
-      for (int j = 0; j < ND; ++j) {
-        acc[rb][j] *= alpha;
-        bf16x8 vf = {va[j][0], va[j][1], va[j][2], va[j][3], vb[j][0], vb[j][1], vb[j][2], vb[j][3]};
-        acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[rb][j], 0, 0, 0);
-      }
+      for (int j = 0; j < ND; ++j) acc[rb][j] *= alpha;
     }
   }
-
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    l[rb] += __shfl_xor(l[rb], 16);
-    l[rb] += __shfl_xor(l[rb], 32);
-  }
-
-  // Stage every wave's (m, l, O) in LDS: lane holds O^T[16j + 4grp + e][row col].
+    const float mneg = (m[rb] == -INFINITY) ? 0.f : -m[rb];
+    bf16x8 pf;
+    float ps = 0.f;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[rb][pg][e], c2, mneg));
+        ps += p;
+        pf[4 * pg + e] = (__bf16)p;
+      }
+    l[rb] += ps;
 #pragma unroll
     for (int j = 0; j < ND; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) lds_o[wave][rb * 16 + col][16 * j + 4 * grp + e] = acc[rb][j][e];
-    if (grp == 0) {
-      lds_ml[wave][rb * 16 + col][0] = m[rb];
-      lds_ml[wave][rb * 16 + col][1] = l[rb];
-    }
+      acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v[j], pf, acc[rb][j], 0, 0, 0);
   }
-  __syncthreads();
+}
 
-  const int G = a.G;
-  u16* outp = (u16*)a.out;
-  const size_t slot = (size_t)pair * a.maxc + chunk;
-  // Merge the page-walking waves of each row group.
-  for (int idx = tid; idx < ROWS * D; idx += 256) {
-    const int row = idx / D, d = idx % D;
-    const int rg = row / 32, rr = row % 32;
-    float M = -INFINITY;
+// Finds the sequence holding unit u with a wave-wide scan over ctx_lens;
+// returns it with its first unit in *ub and its clamped context in *ctx_out.
+// Every lane returns the same values.
+__device__ inline int locate_seq(const AttnArgs& a, int64_t u, int64_t* ub, int* ctx_out) {
+  const int lane = threadIdx.x & 63;
+  int64_t base = 0;
+  for (int blk = 0; blk * 64 < a.B; ++blk) {
+    const int b = blk * 64 + lane;
+    const int ctx = b < a.B ? clamp_ctx(a, a.ctx_lens[b], false) : a.R;
+    const int64_t units = b < a.B ? (int64_t)pages_of(ctx) * a.Hkv : 0;
+    int64_t incl = units;
 #pragma unroll
-    for (int w = 0; w < WK; ++w) M = fmaxf(M, lds_ml[w * WR + rg][rr][0]);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < WK; ++w) {
-      const float f = exp2f(lds_ml[w * WR + rg][rr][0] - Mu);
-      L += lds_ml[w * WR + rg][rr][1] * f;
-      O += lds_o[w * WR + rg][rr][d] * f;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
     }
-    if (nch == 1) {
-      if (row < a.RG) {
-        const int r = row / G, g = row % G;
-        outp[(((size_t)b * a.R + r) * a.Hq + (size_t)kvh * G + g) * D + d] = f32_to_bf16_rne(O / L);
+    const int64_t total = __shfl(incl, 63);
+    if (u < base + total) {
+      const int64_t excl = incl - units;
+      const unsigned long long hit = __ballot(base + excl <= u && u < base + incl);
+      const int src = __ffsll((long long)hit) - 1;
+      *ub = base + __shfl(excl, src);
+      *ctx_out = __shfl(ctx, src);
+      return blk * 64 + src;
+    }
+    base += total;
+  }
+  *ub = base;
+  *ctx_out = a.R;
+  return a.B;
+}
+
+// Total units of the batch (same clamping as the kernels), on every lane.
+__device__ inline int64_t total_units_wave(const AttnArgs& a) {
+  const int lane = threadIdx.x & 63;
+  int64_t s = 0;
+  for (int b = lane; b < a.B; b += 64)
+    s += (int64_t)pages_of(clamp_ctx(a, a.ctx_lens[b], false)) * a.Hkv;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  return s;
+}
+
+// Units per lane: equal contiguous runs of at least kMinRunPages.
+__device__ inline int64_t run_length(int64_t total, int nlanes) {
+  const int64_t r = (total + nlanes - 1) / nlanes;
+  return r < kMinRunPages ? kMinRunPages : r;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 streaming kernel
+// ---------------------------------------------------------------------------
+template <int D, int WR>
+__global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
+  constexpr int NC = D / 32;  // K-dim steps of the QK product
+  constexpr int ND = D / 16;  // 16-wide d blocks of the PV product
+  constexpr int WK = 4 / WR;  // independent lanes per work-group
+  constexpr int ROWS = 32 * WR;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rgrp = wave % WR;
+  const int wl = blockIdx.x * WK + wave / WR;  // this wave-lane
+  const int col = lane & 15, grp = lane >> 4;
+
+  // Bad contexts are flagged once, by the first wave of the grid.
+  if (blockIdx.x == 0 && wave == 0)
+    for (int b = lane; b < a.B; b += 64) clamp_ctx(a, a.ctx_lens[b], true);
+
+  const int64_t total = total_units_wave(a);
+  const int64_t span = run_length(total, a.nlanes);
+  int64_t u = (int64_t)wl * span;
+  const int64_t uend = min(u + span, total);
+  if (u >= uend) return;
+
+  int64_t ub;
+  int ctx;
+  int b = locate_seq(a, u, &ub, &ctx);
+  int np = pages_of(ctx);
+  int h = (int)((u - ub) / np);
+
+  const u16* qb = (const u16*)a.q;
+  const u16* kvb = (const u16*)a.kv;
+  const size_t page_elems = (size_t)2 * a.Hkv * kPage * D;
+  const size_t v_off = (size_t)a.Hkv * kPage * D;
+  u16* outp = (u16*)a.out;
+  bool first_seg = true;
+
+  while (u < uend) {
+    const int64_t pair_start = ub + (int64_t)h * np;
+    const int p0 = (int)(u - pair_start);
+    const int p1 = (int)min<int64_t>(np, p0 + (uend - u));
+    const int nseg = p1 - p0;
+    const bool whole = (p0 == 0 && p1 == np);
+    const size_t head_off = (size_t)h * kPage * D;
+    const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+
+    // Query fragments (B operand of S^T = K Q^T): row = lane's column, eight
+    // consecutive d per lane; k-step c covers d chunk 4c + grp.
+    bf16x8 qf[2][NC];
+    int pos[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int i = rgrp * 32 + rb * 16 + col;
+      const bool valid = i < a.RG;
+      const int r = valid ? i / a.G : a.R - 1;
+      const int g = valid ? i % a.G : 0;
+      pos[rb] = ctx - a.R + r;
+      const u16* qp = qb + (((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint4 v = valid ? *(const uint4*)(qp + 8 * (4 * c + grp)) : make_uint4(0, 0, 0, 0);
+        qf[rb][c] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    float m[2] = {-INFINITY, -INFINITY};
+    float l[2] = {0.f, 0.f};
+    f32x4 acc[2][ND];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int j = 0; j < ND; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Two-page steps.  Every prefetch is issued unconditionally (so the
+    // compiler waits for exactly one buffer at a time); a prefetch past the
+    // end re-reads the last step (a cache hit) and its compute is masked.
+    // The scheduling barriers keep each prefetch ahead of the compute it
+    // must overlap.
+    const int nsteps = (nseg + 1) / 2;
+    const int last = nsteps - 1;
+    const int nrun = nsteps + (nsteps & 1);
+    const int minpos = ctx - a.R;  // every row sees tokens up to here
+    auto page_id = [&](int p) {
+      int id = pt[p];
+      if ((unsigned)id >= (unsigned)a.num_pages) {
+        flag(a.status, kBadPage);
+        id = 0;
+      }
+      return id;
+    };
+    auto issue = [&](KVFrag<D>& f, int st) {
+      const int pa = p0 + 2 * min(st, last);
+      const int ida = page_id(pa);
+      const int idb = pa + 1 < p1 ? page_id(pa + 1) : ida;
+      load_step<D>(f, kvb + (size_t)ida * page_elems + head_off,
+                   kvb + (size_t)idb * page_elems + head_off, v_off, lane);
+    };
+    auto run = [&](const KVFrag<D>& f, int st) {
+      const int pa = p0 + 2 * st;
+      const bool valid = st < nsteps;
+      const bool hasb = valid && pa + 1 < p1;
+      const int t0 = pa * kPage;
+      if (hasb && t0 + 2 * kPage - 1 <= minpos)
+        compute_step<D, false>(f, qf, pos, t0 + 4 * grp, true, true, a.scale_log2, m, l, acc);
+      else
+        compute_step<D, true>(f, qf, pos, t0 + 4 * grp, valid, hasb, a.scale_log2, m, l, acc);
+    };
+    KVFrag<D> f0, f1;
+    issue(f0, 0);
+    for (int st = 0; st < nrun; st += 2) {
+      issue(f1, st + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      run(f0, st);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(f0, st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      run(f1, st + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Row sums: every lane holds a partial over its tokens.
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      l[rb] += __shfl_xor(l[rb], 16);
+      l[rb] += __shfl_xor(l[rb], 32);
+    }
+
+    if (whole) {
+      // lane holds O^T[16j + 4grp + e][row col]: four consecutive d values.
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int i = rgrp * 32 + rb * 16 + col;
+        if (i < a.RG) {
+          const int r = i / a.G, g = i % a.G;
+          const float il = 1.f / l[rb];
+          u16* op = outp + (((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D + 4 * grp;
+#pragma unroll
+          for (int j = 0; j < ND; ++j) {
+            const unsigned lo = f32_to_bf16_rne(acc[rb][j][0] * il) |
+                                ((unsigned)f32_to_bf16_rne(acc[rb][j][1] * il) << 16);
+            const unsigned hi = f32_to_bf16_rne(acc[rb][j][2] * il) |
+                                ((unsigned)f32_to_bf16_rne(acc[rb][j][3] * il) << 16);
+            *(uint2*)(op + 16 * j) = make_uint2(lo, hi);
+          }
+        }
       }
     } else {
-      a.part_o[slot * (size_t)ROWS * D + idx] = O;
-      if (d == 0) a.part_ml[slot * ROWS + row] = make_float2(M, L);
+      const size_t slot = (size_t)wl * 2 + (first_seg ? 0 : 1);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = rgrp * 32 + rb * 16 + col;
+        float* po = a.part_o + (slot * ROWS + row) * D + 4 * grp;
+#pragma unroll
+        for (int j = 0; j < ND; ++j)
+          *(float4*)(po + 16 * j) =
+              make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
+        if (grp == 0) a.part_ml[slot * ROWS + row] = make_float2(m[rb], l[rb]);
+      }
     }
-  }
-  if (nch == 1) return;
 
-  // Last work-group of this pair merges the chunk partials in chunk order.
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(&a.counters[pair], 1u);
-    lds_last = (prev == (unsigned)(nch - 1));
-  }
-  __syncthreads();
-  if (!lds_last) return;
-  __threadfence();
-  const size_t base = (size_t)pair * a.maxc;
-  for (int idx = tid; idx < ROWS * D; idx += 256) {
-    const int row = idx / D, d = idx % D;
-    if (row >= a.RG) continue;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, a.part_ml[(base + c) * ROWS + row].x);
-    float L = 0.f, O = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float2 ml = a.part_ml[(base + c) * ROWS + row];
-      const float f = exp2f(ml.x - M);
-      L += ml.y * f;
-      O += a.part_o[(base + c) * (size_t)ROWS * D + idx] * f;
+    // Next segment: the next KV head, or the next sequence.
+    u += nseg;
+    first_seg = false;
+    if (u < uend) {
+      if (++h == a.Hkv) {
+        h = 0;
+        ub += (int64_t)np * a.Hkv;
+        ++b;
+        ctx = clamp_ctx(a, a.ctx_lens[b], false);
+        np = pages_of(ctx);
+      }
     }
-    const int r = row / G, g = row % G;
-    outp[(((size_t)b * a.R + r) * a.Hq + (size_t)kvh * G + g) * D + d] = f32_to_bf16_rne(O / L);
   }
-  if (tid == 0) a.counters[pair] = 0u;
+}
+
+// Combines the partial segments of (b, h) pairs that were split across
+// wave-lanes, in unit order.  One work-group per pair; pairs written whole by
+// one lane exit at once.
+template <int D, int WR>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  constexpr int ROWS = 32 * WR;
+  __shared__ int64_t sh_sum[4][2];
+  __shared__ float sh_M[ROWS], sh_iL[ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pair = blockIdx.x;
+  const int b = pair / a.Hkv, h = pair % a.Hkv;
+
+  // Units before sequence b and in the whole batch.
+  int64_t before = 0, total = 0;
+  for (int s = tid; s < a.B; s += 256) {
+    const int64_t units = (int64_t)pages_of(clamp_ctx(a, a.ctx_lens[s], false)) * a.Hkv;
+    total += units;
+    if (s < b) before += units;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    before += __shfl_xor(before, off);
+    total += __shfl_xor(total, off);
+  }
+  if (lane == 0) {
+    sh_sum[wave][0] = before;
+    sh_sum[wave][1] = total;
+  }
+  __syncthreads();
+  before = sh_sum[0][0] + sh_sum[1][0] + sh_sum[2][0] + sh_sum[3][0];
+  total = sh_sum[0][1] + sh_sum[1][1] + sh_sum[2][1] + sh_sum[3][1];
+  const int np = pages_of(clamp_ctx(a, a.ctx_lens[b], false));
+  const int64_t start = before + (int64_t)h * np;
+  const int64_t span = run_length(total, a.nlanes);
+  const int wa = (int)(start / span), wb = (int)((start + np - 1) / span);
+  if (wa == wb) return;  // one lane held the whole pair and wrote the output
+
+  // Piece k comes from lane wa + k in slot 0, except that the first piece is
+  // in slot 1 when the pair starts inside lane wa's run.
+  const int npieces = wb - wa + 1;
+  const int slot0 = (start == (int64_t)wa * span) ? 0 : 1;
+  auto slot_of = [&](int k) { return (size_t)(wa + k) * 2 + (k == 0 ? slot0 : 0); };
+  if (tid < ROWS) {
+    float M = -INFINITY;
+    for (int k = 0; k < npieces; ++k) M = fmaxf(M, a.part_ml[slot_of(k) * ROWS + tid].x);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+    for (int k = 0; k < npieces; ++k) {
+      const float2 ml = a.part_ml[slot_of(k) * ROWS + tid];
+      L += ml.y * exp2f(ml.x - Mu);
+    }
+    sh_M[tid] = Mu;
+    sh_iL[tid] = 1.f / L;
+  }
+  __syncthreads();
+  u16* outp = (u16*)a.out;
+  for (int idx = tid; idx < a.RG * D; idx += 256) {
+    const int row = idx / D, d = idx % D;
+    const float Mu = sh_M[row];
+    float O = 0.f;
+    for (int k = 0; k < npieces; ++k) {
+      const size_t s = slot_of(k);
+      O += a.part_o[(s * ROWS + row) * D + d] * exp2f(a.part_ml[s * ROWS + row].x - Mu);
+    }
+    const int r = row / a.G, g = row % a.G;
+    outp[(((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D + d] =
+        f32_to_bf16_rne(O * sh_iL[row]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -319,9 +506,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int E = D / 64;  // d values per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pair = blockIdx.x;
-  if (pair >= a.npairs) return;
   const int b = pair / a.Hkv, kvh = pair % a.Hkv;
-  const int ctx = load_ctx(a, b);
+  const int ctx = clamp_ctx(a, a.ctx_lens[b], tid == 0 && kvh == 0);
   const float* qf = (const float*)a.q;
   const float* kv = (const float*)a.kv;
   float* outp = (float*)a.out;
@@ -329,6 +515,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const size_t head_off = (size_t)kvh * kPage * D;
   const size_t v_off = (size_t)a.Hkv * kPage * D;
   const float scale = a.scale_log2;
+  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
 
   for (int i = wave; i < a.RG; i += 4) {
     const int r = i / a.G, g = i % a.G;
@@ -342,7 +529,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     }
     float m = -INFINITY, l = 0.f;
     for (int t = 0; t <= pos; ++t) {
-      const int phys = load_page(a, b, t / kPage);
+      int phys = pt[t / kPage];
+      if ((unsigned)phys >= (unsigned)a.num_pages) {
+        flag(a.status, kBadPage);
+        phys = 0;
+      }
       const int s = t % kPage;
       const float* blk = kv + (size_t)phys * page_elems + head_off;
       float dot = 0.f;
@@ -370,9 +561,37 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// Work-groups the streaming kernel keeps resident on this device (queried
+// once per device): every CU times the kernel's occupancy.
 template <int D, int WR>
-int32_t launch_bf16(const AttnArgs& args, const AttnPlan& ap, hipStream_t s) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, WR>), dim3((unsigned)ap.grid), dim3(256), 0, s, args);
+int stream_grid(int device) {
+  static int cached[64] = {0};
+  if (device < 0 || device >= 64) device = 0;
+  if (cached[device]) return cached[device];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_stream_kernel<D, WR>, 256, 0) !=
+          hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  int g = cus * per_cu;
+  const int cap = kMaxWaves / 4;
+  if (g > cap) g = cap;
+  cached[device] = g;
+  return g;
+}
+
+template <int D, int WR>
+int32_t launch_stream(AttnArgs a, hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return IDLM_ERR_HIP;
+  const int grid = stream_grid<D, WR>(dev);
+  a.nlanes = grid * (4 / WR);
+  hipLaunchKernelGGL((attn_stream_kernel<D, WR>), dim3(grid), dim3(256), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
+  hipLaunchKernelGGL((attn_merge_kernel<D, WR>), dim3(a.B * a.Hkv), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
@@ -391,7 +610,6 @@ int32_t launch_paged_attn(const idlm_isd_dims& d, const Plan& p, const void* q, 
   a.out = out;
   a.part_o = (float*)(ws + p.off_attn_o);
   a.part_ml = (float2*)(ws + p.off_attn_ml);
-  a.counters = (unsigned*)(ws + p.off_attn_cnt);
   a.status = (int32_t*)(ws + p.off_status);
   a.B = d.B;
   a.R = ap.R;
@@ -399,12 +617,10 @@ int32_t launch_paged_attn(const idlm_isd_dims& d, const Plan& p, const void* q, 
   a.Hkv = d.Hkv;
   a.G = ap.G;
   a.RG = ap.RG;
+  a.D = d.D;
   a.max_pages = d.max_pages;
   a.num_pages = d.num_pages;
-  a.CP = ap.CP;
-  a.maxc = ap.maxc;
-  a.npairs = ap.npairs;
-  a.ppx = ap.ppx;
+  a.nlanes = 0;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.D));
   if (d.qkv_dtype == IDLM_F32) {
     if (d.D == 64)
@@ -414,13 +630,13 @@ int32_t launch_paged_attn(const idlm_isd_dims& d, const Plan& p, const void* q, 
     return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
   }
   if (d.D == 64) {
-    if (ap.WR == 1) return launch_bf16<64, 1>(a, ap, s);
-    if (ap.WR == 2) return launch_bf16<64, 2>(a, ap, s);
-    return launch_bf16<64, 4>(a, ap, s);
+    if (ap.WR == 1) return launch_stream<64, 1>(a, s);
+    if (ap.WR == 2) return launch_stream<64, 2>(a, s);
+    return launch_stream<64, 4>(a, s);
   }
-  if (ap.WR == 1) return launch_bf16<128, 1>(a, ap, s);
-  if (ap.WR == 2) return launch_bf16<128, 2>(a, ap, s);
-  return launch_bf16<128, 4>(a, ap, s);
+  if (ap.WR == 1) return launch_stream<128, 1>(a, s);
+  if (ap.WR == 2) return launch_stream<128, 2>(a, s);
+  return launch_stream<128, 4>(a, s);
 }
 
 }  // namespace idlm

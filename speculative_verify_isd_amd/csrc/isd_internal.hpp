@@ -12,20 +12,19 @@ namespace idlm {
 
 constexpr int kPage = 16;
 constexpr int kSub = 2048;  // acceptance sub-chunk: 256 threads x 8 elements
+constexpr int kMaxWaves = 2048;   // streaming-attention waves resident at once (upper bound)
+constexpr int kMinRunPages = 8;   // shortest run of pages given to one wave-lane
 
 // Sticky device status bits (workspace word 0).
 enum : int32_t { kBadPage = 1, kBadCtx = 2, kBadDraft = 4 };
 
-// How one attention launch is cut into work-groups.
+// Attention sizes derived from the dims.
 struct AttnPlan {
   int R, G, RG;   // step rows, heads per KV head, query rows per (b, kv head)
-  int WR;         // waves sharing a page set, one per 32 query rows (1, 2 or 4)
+  int WR;         // waves sharing a run, one per 32 query rows (1, 2 or 4)
   int RGp;        // RG padded to 32 * WR
-  int CP;         // pages per context chunk (split-K unit), multiple of 8
-  int maxc;       // chunks of the longest possible context
   int npairs;     // B * Hkv
-  int ppx;        // (b, kv head) pairs per XCD slot: ceil(npairs / 8)
-  int64_t grid;   // work-groups launched
+  int max_lanes;  // wave-lanes the partial-state slots are sized for
 };
 
 // How one acceptance launch is cut.
