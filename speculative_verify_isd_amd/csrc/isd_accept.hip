@@ -9,25 +9,26 @@
 // guarantee holds) and the committed prefix ends there; with every draft
 // kept, the last clean row supplies a bonus token.
 //
-// Two launches, both HBM streams over bfloat16/float32 logits:
+// Three launches; kernel boundaries are the only synchronisation (no
+// atomics, no fences), and every reduction runs in a fixed order, so results
+// do not depend on scheduling:
 //
-//   accept_stats  grid = B * R * S1.  Each work-group reduces one slice of
-//                 one logit row to (raw max m, sum of exp2((l - m) c)) with
-//                 c = log2(e)/T; exponentials in float32, sums in float64.
-//                 The last work-group of a sequence (atomic counter) merges
-//                 the slices in fixed order, evaluates p_i(x_i) and q_i(x_i)
-//                 in float64, draws the Philox uniforms, runs the sequential
-//                 ratio test and writes the kept prefix plus a sampling plan.
-//   accept_sample grid = B * S2.  Each work-group forms the sampling weights
-//                 w (residual or bonus row) over its 2048-element
-//                 sub-chunks and stores each sub-chunk's float64 sum.  The
-//                 last work-group of a sequence prefixes those sums in order,
-//                 finds the sub-chunk holding t = u' * sum(w), recomputes it
-//                 and scans it to the token: the smallest v whose running sum
-//                 exceeds t.
-//
-// Every merge runs in a fixed order, so results do not depend on scheduling.
-// Counters return to zero after use.
+//   accept_stats       grid B*R*S1.  Each work-group reduces one slice of one
+//                      logit row to (raw max m, sum of exp2((l - m) c)) with
+//                      c = log2(e)/T: every load of the slice is issued before
+//                      any arithmetic, exponentials in float32, sums in
+//                      float64.  Greedy (T = 0): (max, lowest argmax).
+//   accept_decide_sum  grid B*S2.  Each work-group recomputes its sequence's
+//                      decision from the slice statistics (row merge, p_i(x_i)
+//                      and q_i(x_i) in float64, Philox uniforms, sequential
+//                      ratio test), then sums the sampling weights (residual
+//                      max(0, p_j - q_j) or bonus p) of its 2048-element
+//                      sub-chunks.  Its first work-group writes the kept
+//                      prefix, the accept length and the plan.
+//   accept_select      grid B.  Prefixes the sub-chunk sums in order, finds
+//                      the sub-chunk holding t = u' * sum(w), recomputes it
+//                      bit for bit and scans it to the smallest v whose
+//                      running sum exceeds t.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -83,11 +84,9 @@ struct AccArgs {
   double* debug;
   int32_t* status;
   double2* stats;   // [B][R][S1]: (m, s) or, greedy, (best value, best index)
-  unsigned* cnt1;   // [B]
-  unsigned* cnt2;   // [B]
   SamplePlan* plan; // [B]
   double* subsum;   // [B][nsub]
-  int B, N, K, R, V, S1, chunk1, nsub, spw, S2, f32, vec_ok;
+  int B, N, K, R, V, S1, nsub, spw, S2, f32, vec_ok;
 };
 
 // Row rho of sequence b: rho < N is clean row rho, otherwise MASK row rho - N.
@@ -101,8 +100,7 @@ __device__ inline float load1(const void* row, int v, int f32) {
   return f32 ? ((const float*)row)[v] : __uint_as_float(((unsigned)((const u16*)row)[v]) << 16);
 }
 
-// Eight consecutive logits starting at v (< hi); elements at or past hi read
-// as -inf.
+// Eight consecutive logits starting at v; elements at or past hi read as -inf.
 __device__ inline void load8(const void* row, int v, int hi, int f32, int vec_ok, float x[8]) {
   if (vec_ok && v + 8 <= hi) {
     if (f32) {
@@ -125,31 +123,12 @@ __device__ inline void load8(const void* row, int v, int hi, int f32, int vec_ok
   for (int e = 0; e < 8; ++e) x[e] = (v + e < hi) ? load1(row, v + e, f32) : -INFINITY;
 }
 
-// Greedy reduction: larger value wins, lower index on ties.
+// Greedy order: larger value wins, lower index on ties.
 __device__ inline void better(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) {
     bv = v;
     bi = i;
   }
-}
-
-__device__ inline void wg_argmax(float& bv, int& bi, float* sh_v, int* sh_i) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float vo = __shfl_xor(bv, off);
-    const int io = __shfl_xor(bi, off);
-    better(bv, bi, vo, io);
-  }
-  if (lane == 0) {
-    sh_v[wave] = bv;
-    sh_i[wave] = bi;
-  }
-  __syncthreads();
-  bv = sh_v[0];
-  bi = sh_i[0];
-  for (int w = 1; w < 4; ++w) better(bv, bi, sh_v[w], sh_i[w]);
-  __syncthreads();
 }
 
 // Inclusive scan of one double per thread over the work-group; every
@@ -170,208 +149,236 @@ __device__ inline void wg_scan_incl(double x, double* sh_wave, double* sh_incl) 
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: row statistics, then the ratio test in the sequence's last WG.
+// Kernel 1: row-slice statistics.
 // ---------------------------------------------------------------------------
+template <int U>
 __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
   __shared__ double sh_s[4];
   __shared__ float sh_m[4];
   __shared__ int sh_i[4];
-  __shared__ double row_m[32], row_s[32];
-  __shared__ int is_last;
-
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t wg = blockIdx.x;
   const int c = (int)(wg % a.S1);
   const int64_t tmp = wg / a.S1;
   const int rho = (int)(tmp % a.R);
   const int b = (int)(tmp / a.R);
   const void* row = row_ptr(a, b, rho);
-  const int lo = c * a.chunk1;
-  const int hi = min(a.V, lo + a.chunk1);
+  const int lo = c * kSub * U;
+  const int hi = min(a.V, lo + kSub * U);
 
+  // All of this thread's loads first, then the arithmetic.
+  float x[U][8];
+#pragma unroll
+  for (int k = 0; k < U; ++k) load8(row, lo + k * kSub + 8 * tid, hi, a.f32, a.vec_ok, x[k]);
+
+  double2 res;
   if (a.greedy) {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int v = lo + 8 * tid; v < hi; v += 8 * 256) {
-      float x[8];
-      load8(row, v, hi, a.f32, a.vec_ok, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (v + e < hi) better(bv, bi, x[e], v + e);
+    for (int k = 0; k < U; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int v = lo + k * kSub + 8 * tid + e;
+        if (v < hi) better(bv, bi, x[k][e], v);
+      }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float vo = __shfl_xor(bv, off);
+      const int io = __shfl_xor(bi, off);
+      better(bv, bi, vo, io);
     }
-    wg_argmax(bv, bi, sh_m, sh_i);
-    if (tid == 0) a.stats[((size_t)b * a.R + rho) * a.S1 + c] = make_double2(bv, (double)bi);
+    if (lane == 0) {
+      sh_m[wave] = bv;
+      sh_i[wave] = bi;
+    }
+    __syncthreads();
+    if (tid != 0) return;
+    bv = sh_m[0];
+    bi = sh_i[0];
+    for (int w = 1; w < 4; ++w) better(bv, bi, sh_m[w], sh_i[w]);
+    res = make_double2((double)bv, (double)bi);
   } else {
     float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, x[k][e]);
     double s = 0.0;
-    for (int v = lo + 8 * tid; v < hi; v += 8 * 256) {
-      float x[8];
-      load8(row, v, hi, a.f32, a.vec_ok, x);
-      float mx = x[0];
+    if (m != -INFINITY) {
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      if (mx > m) {
-        if (m != -INFINITY) s *= exp2((double)(m - mx) * (double)a.c2);
-        m = mx;
+      for (int k = 0; k < U; ++k) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += exp2f((x[k][e] - m) * a.c2);
+        s += (double)part;
       }
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part += exp2f((x[e] - m) * a.c2);
-      s += (double)part;
     }
     // Work-group merge; m is a raw logit, so rescale with the same c2.
-    {
-      const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float mo = __shfl_xor(m, off);
-        const double so = __shfl_xor(s, off);
-        const float M = fmaxf(m, mo);
-        if (M != -INFINITY)
-          s = s * exp2((double)(m - M) * a.c2) + so * exp2((double)(mo - M) * a.c2);
-        m = M;
-      }
-      if (lane == 0) {
-        sh_m[wave] = m;
-        sh_s[wave] = s;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        float M = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
-        double S = 0.0;
-        for (int w = 0; w < 4; ++w)
-          if (sh_m[w] != -INFINITY) S += sh_s[w] * exp2((double)(sh_m[w] - M) * a.c2);
-        a.stats[((size_t)b * a.R + rho) * a.S1 + c] = make_double2((double)M, S);
-      }
+    for (int off = 32; off > 0; off >>= 1) {
+      const float mo = __shfl_xor(m, off);
+      const double so = __shfl_xor(s, off);
+      const float M = fmaxf(m, mo);
+      if (M != -INFINITY)
+        s = (m == -INFINITY ? 0.0 : s * exp2((double)(m - M) * a.c2)) +
+            (mo == -INFINITY ? 0.0 : so * exp2((double)(mo - M) * a.c2));
+      m = M;
     }
+    if (lane == 0) {
+      sh_m[wave] = m;
+      sh_s[wave] = s;
+    }
+    __syncthreads();
+    if (tid != 0) return;
+    const float M = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
+    double S = 0.0;
+    for (int w = 0; w < 4; ++w)
+      if (sh_m[w] != -INFINITY) S += sh_s[w] * exp2((double)(sh_m[w] - M) * a.c2);
+    res = make_double2((double)M, S);
   }
+  a.stats[((size_t)b * a.R + rho) * a.S1 + c] = res;
+}
 
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(&a.cnt1[b], 1u);
-    is_last = (prev == (unsigned)(a.R * a.S1 - 1));
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // ---- finalisation for sequence b (one work-group) ----
-  if (tid < a.R) {
-    const double2* st = a.stats + ((size_t)b * a.R + tid) * a.S1;
+// ---------------------------------------------------------------------------
+// The sequence's decision, recomputed by every work-group that needs it.
+// Collective: all 256 threads call it.  Leaves the plan in *out_plan, the
+// draft count in *out_kp, the per-draft (p, q, u, u') in sh_draft and the
+// raw draft ids in sh_ids.
+// ---------------------------------------------------------------------------
+__device__ void decide(const AccArgs& a, int b, SamplePlan* out_plan, int* out_kp,
+                       double (*sh_draft)[4], double* sh_m, double* sh_s, int* sh_ids) {
+  const int tid = threadIdx.x;
+  const int R = a.R, N = a.N, K = a.K;
+  // Row merge: thread rho walks its S1 slices in order.
+  if (tid < R) {
+    const double2* st = a.stats + ((size_t)b * R + tid) * a.S1;
     if (a.greedy) {
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
-      for (int k = 0; k < a.S1; ++k) better(bv, bi, (float)st[k].x, (int)st[k].y);
-      row_m[tid] = bv;
-      row_s[tid] = (double)bi;
+      for (int k = 0; k < a.S1; ++k) {
+        const double2 v = st[k];
+        better(bv, bi, (float)v.x, (int)v.y);
+      }
+      sh_m[tid] = bv;
+      sh_s[tid] = (double)bi;
     } else {
       double M = -INFINITY;
       for (int k = 0; k < a.S1; ++k) M = fmax(M, st[k].x);
       double S = 0.0;
-      for (int k = 0; k < a.S1; ++k)
-        if (st[k].x != -INFINITY) S += st[k].y * exp2((st[k].x - M) * (double)a.c2);
-      row_m[tid] = M;
-      row_s[tid] = S;
+      for (int k = 0; k < a.S1; ++k) {
+        const double2 v = st[k];
+        if (v.x != -INFINITY) S += v.y * exp2((v.x - M) * (double)a.c2);
+      }
+      sh_m[tid] = M;
+      sh_s[tid] = S;
+    }
+  }
+  if (tid < K) sh_ids[tid] = a.drafts[(size_t)b * K + tid];
+  __syncthreads();
+  // Per-draft inputs of the ratio test, one thread per draft.
+  if (tid < K) {
+    bool listed = true;  // no -1 terminator before this draft
+    for (int i = 0; i <= tid; ++i) listed = listed && (sh_ids[i] >= 0);
+    if (listed) {
+      const int x = min(sh_ids[tid], a.V - 1);  // out-of-range ids are flagged
+      const U64x4 w = philox4x64_10((uint64_t)tid, 0, 0, 0, a.seed, (uint64_t)b);
+      double p, q;
+      if (a.greedy) {
+        p = (x == (int)sh_s[tid]) ? 1.0 : 0.0;
+        q = (x == (int)sh_s[N + tid]) ? 1.0 : 0.0;
+      } else {
+        const double lp = (double)load1(row_ptr(a, b, tid), x, a.f32);
+        const double lq = (double)load1(row_ptr(a, b, N + tid), x, a.f32);
+        p = exp((lp - sh_m[tid]) * a.invT) / sh_s[tid];
+        q = exp((lq - sh_m[N + tid]) * a.invT) / sh_s[N + tid];
+      }
+      sh_draft[tid][0] = p;
+      sh_draft[tid][1] = q;
+      sh_draft[tid][2] = top24(w.w[0]);
+      sh_draft[tid][3] = top24(w.w[1]);
     }
   }
   __syncthreads();
   if (tid == 0) {
-    const int K = a.K, N = a.N;
-    const int32_t* dr = a.drafts + (size_t)b * K;
     int kp = K;
-    for (int i = 0; i < K; ++i) {
-      const int x = dr[i];
-      if (x < 0) {
-        if (x != -1) atomicOr(a.status, kBadDraft);
+    for (int i = 0; i < K; ++i)
+      if (sh_ids[i] < 0) {
         kp = i;
         break;
       }
-    }
-    double* dbg = a.debug ? a.debug + (size_t)b * (N + 1) * 4 : nullptr;
-    if (dbg)
-      for (int i = 0; i < 4 * (N + 1); ++i) dbg[i] = NAN;
     int j = kp;
     for (int i = 0; i < kp; ++i) {
-      int x = dr[i];
-      if (x >= a.V) {
-        atomicOr(a.status, kBadDraft);
-        x = a.V - 1;
-      }
-      const U64x4 w = philox4x64_10((uint64_t)i, 0, 0, 0, a.seed, (uint64_t)b);
-      const double u = top24(w.w[0]), u2 = top24(w.w[1]);
-      double p, q;
-      if (a.greedy) {
-        p = (x == (int)row_s[i]) ? 1.0 : 0.0;
-        q = (x == (int)row_s[N + i]) ? 1.0 : 0.0;
-      } else {
-        const double lp = (double)load1(row_ptr(a, b, i), x, a.f32);
-        const double lq = (double)load1(row_ptr(a, b, N + i), x, a.f32);
-        p = exp((lp - row_m[i]) * a.invT) / row_s[i];
-        q = exp((lq - row_m[N + i]) * a.invT) / row_s[N + i];
-      }
-      if (dbg) {
-        dbg[4 * i + 0] = p;
-        dbg[4 * i + 1] = q;
-        dbg[4 * i + 2] = u;
-        dbg[4 * i + 3] = u2;
-      }
+      const double p = sh_draft[i][0], q = sh_draft[i][1], u = sh_draft[i][2];
       if (!(p >= q || u * q < p)) {
         j = i;
         break;
       }
     }
-    int32_t* ot = a.out_tokens + (size_t)b * N;
-    for (int i = 0; i < N; ++i) ot[i] = (i < j) ? dr[i] : -1;
-    a.out_len[b] = j + 1;
-    const U64x4 wj = philox4x64_10((uint64_t)j, 0, 0, 0, a.seed, (uint64_t)b);
     SamplePlan sp;
     sp.j = j;
-    sp.u2 = top24(wj.w[1]);
+    sp.u2 = j < kp ? sh_draft[j][3]
+                   : top24(philox4x64_10((uint64_t)j, 0, 0, 0, a.seed, (uint64_t)b).w[1]);
     sp.row_p = j;
     sp.row_q = (j < kp) ? j : 0;
-    sp.mode = (j < kp) ? 0 : 1;
-    sp.mp = row_m[j];
-    sp.sp = row_s[j];
-    sp.mq = (j < kp) ? row_m[N + j] : 0.0;
-    sp.sq = (j < kp) ? row_s[N + j] : 1.0;
-    sp.pad = 0.0;
-    if (a.greedy) {
-      // p and q are one-hot: the residual (or its fallback) is the clean argmax.
-      const int tok = (int)row_s[j];
-      ot[j] = tok;
-      sp.mode = 2;
-      if (dbg) {
-        dbg[4 * N + 0] = 1.0;
-        dbg[4 * N + 1] = sp.u2;
-        dbg[4 * N + 2] = sp.u2;
-        dbg[4 * N + 3] = (double)tok;
-      }
+    sp.mode = a.greedy ? 2 : ((j < kp) ? 0 : 1);
+    sp.mp = sh_m[j];
+    sp.sp = sh_s[j];
+    sp.mq = (j < kp) ? sh_m[N + j] : 0.0;
+    sp.sq = (j < kp) ? sh_s[N + j] : 1.0;
+    sp.pad = a.greedy ? sh_s[j] : 0.0;  // greedy: the clean argmax of row j
+    *out_plan = sp;
+    *out_kp = kp;
+  }
+  __syncthreads();
+}
+
+// Writes the kept prefix, accept length, debug rows and (greedy) the token.
+__device__ void write_prefix(const AccArgs& a, int b, const SamplePlan& sp, int kp,
+                             double (*sh_draft)[4], const int* sh_ids) {
+  const int tid = threadIdx.x, N = a.N, j = sp.j;
+  if (tid < N) {
+    int tok = -1;
+    if (tid < j) tok = sh_ids[tid];
+    if (tid == j && sp.mode == 2) tok = (int)sp.pad;
+    a.out_tokens[(size_t)b * N + tid] = tok;
+  }
+  if (tid == 0) {
+    a.out_len[b] = j + 1;
+    for (int i = 0; i < a.K; ++i) {
+      const int x = sh_ids[i];
+      if (x < -1 || x >= a.V) atomicOr(a.status, kBadDraft);
+      if (x < 0) break;
     }
-    a.plan[b] = sp;
-    a.cnt1[b] = 0u;
+  }
+  if (a.debug) {
+    double* dbg = a.debug + (size_t)b * (N + 1) * 4;
+    for (int i = tid; i < 4 * (N + 1); i += 256) {
+      const int r = i / 4, k = i % 4;
+      double v = NAN;
+      if (r < N - 1 && r <= j && r < kp) v = sh_draft[r][k];
+      if (r == N && sp.mode == 2) v = (k == 0) ? 1.0 : (k == 3 ? sp.pad : sp.u2);
+      dbg[i] = v;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: residual / bonus sampling by chunked inverse CDF.
+// Kernel 2: decision + sub-chunk sums of the sampling weights.
 // ---------------------------------------------------------------------------
 
-// Sampling weights of the 8 elements at v (mode 0 residual, 1 p only).
-// Exponentials are float32; the normalisation and the difference p - q are
-// float64, so p and q keep exactly the scales their row sums gave them and
-// the residual carries no systematic float32 scale error.
-__device__ inline void weights8(const AccArgs& a, const SamplePlan& sp, int b, int v, double w[8]) {
+// Sampling weights of 8 elements (mode 0 residual, 1 p only).  Exponentials
+// are float32; the normalisation and the difference p - q are float64, so p
+// and q keep exactly the scales their row sums gave them and the residual
+// carries no systematic float32 scale error.
+__device__ inline void weights8(const AccArgs& a, const SamplePlan& sp, int mode,
+                                const float xp[8], const float xq[8], double w[8]) {
   const float c2 = a.c2;
   const float mp = (float)sp.mp;
   const double ip = 1.0 / sp.sp;
-  float xp[8];
-  load8(row_ptr(a, b, sp.row_p), v, a.V, a.f32, a.vec_ok, xp);
-  if (sp.mode == 0) {
+  if (mode == 0) {
     const float mq = (float)sp.mq;
     const double iq = 1.0 / sp.sq;
-    float xq[8];
-    load8(row_ptr(a, b, a.N + sp.row_q), v, a.V, a.f32, a.vec_ok, xq);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       w[e] = fmax(0.0, (double)exp2f((xp[e] - mp) * c2) * ip - (double)exp2f((xq[e] - mq) * c2) * iq);
@@ -381,75 +388,117 @@ __device__ inline void weights8(const AccArgs& a, const SamplePlan& sp, int b, i
   }
 }
 
-// Weights of one sub-chunk (this thread's 8 in w) and the inclusive scan of
-// the per-thread sums in sh_incl.  Recomputing a sub-chunk reproduces every
-// value bit for bit, so the total stored in the first pass and the scan used
-// to locate t agree exactly.
-__device__ inline void subchunk_scan(const AccArgs& a, const SamplePlan& sp, int b, int sc,
-                                     double w[8], double* sh_wave, double* sh_incl) {
-  const int v = sc * kSub + 8 * threadIdx.x;
-  weights8(a, sp, b, v, w);
+// Thread sums of one sub-chunk and their work-group inclusive scan (total
+// returned).  The same code recomputes a sub-chunk bit for bit in
+// accept_select.
+__device__ inline double subchunk_scan(const AccArgs& a, const SamplePlan& sp, int mode,
+                                       const float xp[8], const float xq[8], double w[8],
+                                       double* sh_wave, double* sh_incl) {
+  weights8(a, sp, mode, xp, xq, w);
   double ts = 0.0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ts += w[e];
   wg_scan_incl(ts, sh_wave, sh_incl);
+  return sh_incl[255];
 }
 
-__global__ __launch_bounds__(256) void accept_sample_kernel(AccArgs a) {
-  __shared__ double sh_wave[4];
-  __shared__ double sh_incl[256];
-  __shared__ int is_last;
-  __shared__ int found_tok, found_last;
-  __shared__ double sh_t, sh_base, sh_W;
-  __shared__ int sh_sc, sh_past;
+// This thread's 8 logits of sub-chunk sc in the p row (and q row, mode 0).
+__device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, int mode, int sc,
+                                float xp[8], float xq[8]) {
+  const int v = sc * kSub + 8 * threadIdx.x;
+  load8(row_ptr(a, b, sp.row_p), v, a.V, a.f32, a.vec_ok, xp);
+  if (mode == 0) {
+    load8(row_ptr(a, b, a.N + sp.row_q), v, a.V, a.f32, a.vec_ok, xq);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xq[e] = -INFINITY;
+  }
+}
 
+constexpr int kMaxSpw = 4;  // upper bound of AcceptPlan::spw
+
+__global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
+  __shared__ double sh_draft[16][4];
+  __shared__ double sh_m[32], sh_s[32];
+  __shared__ int sh_ids[16];
+  __shared__ SamplePlan sh_plan;
+  __shared__ int sh_kp;
+  __shared__ double sh_wave[4], sh_incl[256];
   const int tid = threadIdx.x;
   const int b = (int)(blockIdx.x / a.S2);
   const int w0 = (int)(blockIdx.x % a.S2);
-  SamplePlan sp = a.plan[b];
-  double* subs = a.subsum + (size_t)b * a.nsub;
-  double w[8];
+  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_m, sh_s, sh_ids);
+  const SamplePlan sp = sh_plan;
+  if (w0 == 0) {
+    write_prefix(a, b, sp, sh_kp, sh_draft, sh_ids);
+    if (tid == 0) a.plan[b] = sp;
+  }
+  if (sp.mode == 2) return;  // greedy: nothing to sample
 
   const int sc_lo = w0 * a.spw, sc_hi = min(a.nsub, sc_lo + a.spw);
-  for (int sc = sc_lo; sc < sc_hi; ++sc) {
-    subchunk_scan(a, sp, b, sc, w, sh_wave, sh_incl);
-    if (tid == 0) subs[sc] = sh_incl[255];
-    __syncthreads();
-  }
+  float xp[kMaxSpw][8], xq[kMaxSpw][8];
+#pragma unroll
+  for (int k = 0; k < kMaxSpw; ++k)
+    if (sc_lo + k < sc_hi) load_sub(a, b, sp, sp.mode, sc_lo + k, xp[k], xq[k]);
+  double w[8];
+  double* subs = a.subsum + (size_t)b * a.nsub;
+#pragma unroll
+  for (int k = 0; k < kMaxSpw; ++k)
+    if (sc_lo + k < sc_hi) {
+      const double tot = subchunk_scan(a, sp, sp.mode, xp[k], xq[k], w, sh_wave, sh_incl);
+      if (tid == 0) subs[sc_lo + k] = tot;
+    }
+}
 
+// ---------------------------------------------------------------------------
+// Kernel 3: locate t and scan one sub-chunk.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
+  __shared__ double sh_wave[4], sh_incl[256];
+  __shared__ double sh_sub[kMaxSubChunks];
+  __shared__ double sh_t, sh_base, sh_W;
+  __shared__ int sh_sc, sh_past, sh_mode;
+  __shared__ int found_tok, found_last;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const SamplePlan sp = a.plan[b];
+  if (sp.mode == 2) return;
+  const double* subs = a.subsum + (size_t)b * a.nsub;
+  float xp[8], xq[8];
+  double w[8];
+
+  for (int i = tid; i < a.nsub; i += 256) sh_sub[i] = subs[i];
+  __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(&a.cnt2[b], 1u);
-    is_last = (prev == (unsigned)(a.S2 - 1));
+    double W = 0.0;
+    for (int sc = 0; sc < a.nsub; ++sc) W += sh_sub[sc];
+    sh_W = W;
+    sh_mode = sp.mode;
   }
   __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // ---- last work-group of sequence b: total, locate, scan ----
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    if (tid == 0) {
-      double W = 0.0;
-      for (int sc = 0; sc < a.nsub; ++sc) W += subs[sc];
-      sh_W = W;
+  if (!(sh_W > 0.0)) {
+    // The residual vanished to rounding: fall back to p_j over the whole row.
+    for (int sc = 0; sc < a.nsub; ++sc) {
+      load_sub(a, b, sp, 1, sc, xp, xq);
+      const double tot = subchunk_scan(a, sp, 1, xp, xq, w, sh_wave, sh_incl);
+      if (tid == 0) sh_sub[sc] = tot;
     }
     __syncthreads();
-    if (sh_W > 0.0 || attempt == 1) break;
-    // The residual vanished to rounding: fall back to p_j over the whole row.
-    sp.mode = 1;
-    for (int sc = 0; sc < a.nsub; ++sc) {
-      subchunk_scan(a, sp, b, sc, w, sh_wave, sh_incl);
-      if (tid == 0) subs[sc] = sh_incl[255];
-      __syncthreads();
+    if (tid == 0) {
+      double W = 0.0;
+      for (int sc = 0; sc < a.nsub; ++sc) W += sh_sub[sc];
+      sh_W = W;
+      sh_mode = 1;
     }
+    __syncthreads();
   }
   if (tid == 0) {
     const double t = sp.u2 * sh_W;
     double cum = 0.0, base = 0.0;
     int sel = -1, lastpos = 0;
     for (int sc = 0; sc < a.nsub; ++sc) {
-      const double nx = cum + subs[sc];
-      if (subs[sc] > 0.0) lastpos = sc;
+      const double nx = cum + sh_sub[sc];
+      if (sh_sub[sc] > 0.0) lastpos = sc;
       if (sel < 0 && nx > t) {
         sel = sc;
         base = cum;
@@ -466,8 +515,9 @@ __global__ __launch_bounds__(256) void accept_sample_kernel(AccArgs a) {
   }
   __syncthreads();
   const double t = sh_t, base = sh_base;
-  const int sc = sh_sc;
-  subchunk_scan(a, sp, b, sc, w, sh_wave, sh_incl);
+  const int sc = sh_sc, mode = sh_mode;
+  load_sub(a, b, sp, mode, sc, xp, xq);
+  subchunk_scan(a, sp, mode, xp, xq, w, sh_wave, sh_incl);
   const int v0 = sc * kSub + 8 * tid;
   int lastp = -1;
 #pragma unroll
@@ -505,8 +555,14 @@ __global__ __launch_bounds__(256) void accept_sample_kernel(AccArgs a) {
       dbg[2] = sp.u2;
       dbg[3] = (double)tok;
     }
-    a.cnt2[b] = 0u;
   }
+}
+
+template <int U>
+int32_t launch_stats(const AccArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)a.B * a.R * a.S1;
+  hipLaunchKernelGGL((accept_stats_kernel<U>), dim3((unsigned)g), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
 }  // namespace
@@ -529,8 +585,6 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.debug = out_debug;
   a.status = (int32_t*)(ws + p.off_status);
   a.stats = (double2*)(ws + p.off_stats);
-  a.cnt1 = (unsigned*)(ws + p.off_cnt1);
-  a.cnt2 = (unsigned*)(ws + p.off_cnt2);
   a.plan = (SamplePlan*)(ws + p.off_splan);
   a.subsum = (double*)(ws + p.off_subsum);
   a.B = d.B;
@@ -539,7 +593,6 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.R = ap.R;
   a.V = d.V;
   a.S1 = ap.S1;
-  a.chunk1 = ap.chunk1;
   a.nsub = ap.nsub;
   a.spw = ap.spw;
   a.S2 = ap.S2;
@@ -547,12 +600,21 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   const size_t es = a.f32 ? 4 : 2;
   a.vec_ok = ((size_t)d.V * es) % 16 == 0 && ((uintptr_t)lc % 16) == 0 &&
              (lm == nullptr || ((uintptr_t)lm % 16) == 0);
-  const int64_t g1 = (int64_t)d.B * ap.R * ap.S1;
-  hipLaunchKernelGGL(accept_stats_kernel, dim3((unsigned)g1), dim3(256), 0, s, a);
+  int32_t r;
+  switch (ap.U1) {
+    case 8: r = launch_stats<8>(a, s); break;
+    case 4: r = launch_stats<4>(a, s); break;
+    case 2: r = launch_stats<2>(a, s); break;
+    default: r = launch_stats<1>(a, s); break;
+  }
+  if (r != IDLM_OK) return r;
+  // Greedy needs one decision work-group per sequence and no sampling.
+  if (a.greedy) a.S2 = 1;
+  const int64_t g2 = (int64_t)d.B * a.S2;
+  hipLaunchKernelGGL(accept_decide_sum_kernel, dim3((unsigned)g2), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
   if (a.greedy) return IDLM_OK;
-  const int64_t g2 = (int64_t)d.B * ap.S2;
-  hipLaunchKernelGGL(accept_sample_kernel, dim3((unsigned)g2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(accept_select_kernel, dim3((unsigned)d.B), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 

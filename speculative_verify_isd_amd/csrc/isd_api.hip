@@ -24,6 +24,7 @@ int32_t check_dims(const idlm_isd_dims* d) {
   if (d->logits_dtype != IDLM_BF16 && d->logits_dtype != IDLM_F32) return IDLM_ERR_DIMS;
   if (d->page_size != kPage) return IDLM_ERR_UNSUPPORTED;
   if (d->D != 64 && d->D != 128) return IDLM_ERR_UNSUPPORTED;
+  if ((int64_t)d->V > (int64_t)kSub * kMaxSubChunks) return IDLM_ERR_UNSUPPORTED;
   const int64_t R = 2 * (int64_t)d->N - 1;
   if (R * (d->Hq / d->Hkv) > 128) return IDLM_ERR_UNSUPPORTED;
   if ((int64_t)d->B * d->Hkv > (1 << 24)) return IDLM_ERR_DIMS;
@@ -53,28 +54,29 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   AcceptPlan& c = p->acc;
   c.R = 2 * d.N - 1;
   c.nsub = (int)ceil_div(d.V, kSub);
+  // Stats: the widest per-thread batch that still gives >= 2048 work-groups.
   const int64_t rows = (int64_t)std::max(d.B, 1) * c.R;
-  int S1 = (int)std::min<int64_t>(c.nsub, std::max<int64_t>(1, ceil_div(2048, rows)));
-  const int per = (int)ceil_div(c.nsub, S1);
-  c.chunk1 = per * kSub;
-  c.S1 = (int)ceil_div(d.V, c.chunk1);
-  c.spw = (int)std::min<int64_t>(c.nsub, std::max<int64_t>(1, ceil_div((int64_t)c.nsub * std::max(d.B, 1), 2048)));
+  c.U1 = 1;
+  for (int u = 8; u >= 1; u /= 2)
+    if (rows * ceil_div(d.V, (int64_t)kSub * u) >= 2048) {
+      c.U1 = u;
+      break;
+    }
+  c.S1 = (int)ceil_div(d.V, (int64_t)kSub * c.U1);
+  // Sampling: up to 4 sub-chunks per work-group, aiming at ~2048 work-groups.
+  c.spw = (int)std::min<int64_t>(4, std::max<int64_t>(1, ceil_div((int64_t)c.nsub * std::max(d.B, 1), 2048)));
+  c.spw = std::min(c.spw, c.nsub);
   c.S2 = (int)ceil_div(c.nsub, c.spw);
   // ---- workspace layout ----
   size_t o = 0;
   p->off_status = o;
   o = align256(o + 4);
-  p->off_attn_cnt = o;
   // Streaming attention: two partial-state slots per wave-lane (bf16 path).
   const size_t nslots = d.qkv_dtype == IDLM_BF16 ? (size_t)a.max_lanes * 2 : 0;
   p->off_attn_ml = o;
   o = align256(o + nslots * a.RGp * 8);
   p->off_attn_o = o;
   o = align256(o + nslots * a.RGp * d.D * 4);
-  p->off_cnt1 = o;
-  o = align256(o + (size_t)d.B * 4);
-  p->off_cnt2 = o;
-  o = align256(o + (size_t)d.B * 4);
   p->off_splan = o;
   o = align256(o + (size_t)d.B * sizeof(SamplePlan));
   p->off_stats = o;

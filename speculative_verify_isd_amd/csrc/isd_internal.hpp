@@ -12,6 +12,7 @@ namespace idlm {
 
 constexpr int kPage = 16;
 constexpr int kSub = 2048;  // acceptance sub-chunk: 256 threads x 8 elements
+constexpr int kMaxSubChunks = 1024;  // V <= kSub * kMaxSubChunks
 constexpr int kMaxWaves = 2048;   // streaming-attention waves resident at once (upper bound)
 constexpr int kMinRunPages = 8;   // shortest run of pages given to one wave-lane
 
@@ -31,9 +32,9 @@ struct AttnPlan {
 struct AcceptPlan {
   int R;          // rows per sequence: N clean + K mask
   int nsub;       // kSub-element sub-chunks per row
-  int S1;         // stats work-groups per row
-  int chunk1;     // elements per stats work-group (multiple of kSub)
-  int spw;        // sub-chunks per sampling work-group
+  int U1;         // 16-byte vectors per thread in a stats work-group (1, 2, 4 or 8)
+  int S1;         // stats work-groups per row: ceil(V / (kSub * U1))
+  int spw;        // sub-chunks per sampling work-group (1..4)
   int S2;         // sampling work-groups per sequence
 };
 
@@ -52,8 +53,8 @@ struct SamplePlan {
 struct Plan {
   AttnPlan attn;
   AcceptPlan acc;
-  size_t off_status, off_attn_cnt, off_attn_ml, off_attn_o;
-  size_t off_cnt1, off_cnt2, off_splan, off_stats, off_subsum;
+  size_t off_status, off_attn_ml, off_attn_o;
+  size_t off_splan, off_stats, off_subsum;
   size_t total;
 };
 
