@@ -86,7 +86,7 @@ struct AccArgs {
   double2* stats;   // [B][R][S1]: (m, s) or, greedy, (best value, best index)
   SamplePlan* plan; // [B]
   double* subsum;   // [B][nsub]
-  int B, N, K, R, V, S1, nsub, spw, S2, f32, vec_ok;
+  int B, N, K, R, V, S1, nsub, spw, S2, f32;
 };
 
 // Row rho of sequence b: rho < N is clean row rho, otherwise MASK row rho - N.
@@ -100,16 +100,23 @@ __device__ inline float load1(const void* row, int v, int f32) {
   return f32 ? ((const float*)row)[v] : __uint_as_float(((unsigned)((const u16*)row)[v]) << 16);
 }
 
-// Eight consecutive logits starting at v; elements at or past hi read as -inf.
-__device__ inline void load8(const void* row, int v, int hi, int f32, int vec_ok, float x[8]) {
-  if (vec_ok && v + 8 <= hi) {
-    if (f32) {
-      const float4 p0 = *(const float4*)((const float*)row + v);
-      const float4 p1 = *(const float4*)((const float*)row + v + 4);
+// Eight consecutive logits starting at v; elements at or past hi read as
+// -inf.  VEC (rows 16-byte aligned, V a multiple of 8, so v and hi are
+// multiples of 8): one vector load, from a clamped in-row address when the
+// group lies past hi, with no branch, so a thread's loads can all be in
+// flight together.  Otherwise element by element.
+template <bool VEC, bool F32>
+__device__ inline void load8(const void* row, int v, int hi, float x[8]) {
+  if (VEC) {
+    const bool in = v < hi;
+    const int vi = in ? v : hi - 8;
+    if (F32) {
+      const float4 p0 = *(const float4*)((const float*)row + vi);
+      const float4 p1 = *(const float4*)((const float*)row + vi + 4);
       x[0] = p0.x; x[1] = p0.y; x[2] = p0.z; x[3] = p0.w;
       x[4] = p1.x; x[5] = p1.y; x[6] = p1.z; x[7] = p1.w;
     } else {
-      const uint4 p = *(const uint4*)((const u16*)row + v);
+      const uint4 p = *(const uint4*)((const u16*)row + vi);
       const unsigned w[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -117,10 +124,12 @@ __device__ inline void load8(const void* row, int v, int hi, int f32, int vec_ok
         x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
       }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = in ? x[e] : -INFINITY;
     return;
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = (v + e < hi) ? load1(row, v + e, f32) : -INFINITY;
+  for (int e = 0; e < 8; ++e) x[e] = (v + e < hi) ? load1(row, v + e, F32) : -INFINITY;
 }
 
 // Greedy order: larger value wins, lower index on ties.
@@ -151,7 +160,7 @@ __device__ inline void wg_scan_incl(double x, double* sh_wave, double* sh_incl) 
 // ---------------------------------------------------------------------------
 // Kernel 1: row-slice statistics.
 // ---------------------------------------------------------------------------
-template <int U>
+template <int U, bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
   __shared__ double sh_s[4];
   __shared__ float sh_m[4];
@@ -169,7 +178,7 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
   // All of this thread's loads first, then the arithmetic.
   float x[U][8];
 #pragma unroll
-  for (int k = 0; k < U; ++k) load8(row, lo + k * kSub + 8 * tid, hi, a.f32, a.vec_ok, x[k]);
+  for (int k = 0; k < U; ++k) load8<VEC, F32>(row, lo + k * kSub + 8 * tid, hi, x[k]);
 
   double2 res;
   if (a.greedy) {
@@ -247,12 +256,33 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
 // raw draft ids in sh_ids.
 // ---------------------------------------------------------------------------
 __device__ void decide(const AccArgs& a, int b, SamplePlan* out_plan, int* out_kp,
-                       double (*sh_draft)[4], double* sh_m, double* sh_s, int* sh_ids) {
+                       double (*sh_draft)[4], double* sh_m, double* sh_s, int* sh_ids,
+                       double2* sh_st) {
   const int tid = threadIdx.x;
   const int R = a.R, N = a.N, K = a.K;
+  const int nst = R * a.S1;
+  const bool st_in_lds = nst <= kDecideStats;
+  const double2* st_g = a.stats + (size_t)b * nst;
+  // One round of independent loads: the slice statistics and the drafts.
+  if (st_in_lds)
+    for (int i = tid; i < nst; i += 256) sh_st[i] = st_g[i];
+  if (tid < K) sh_ids[tid] = a.drafts[(size_t)b * K + tid];
+  __syncthreads();
+  // The draft logits (second round) while the rows merge.
+  double lp = 0.0, lq = 0.0;
+  bool listed = false;
+  if (tid < K) {
+    listed = true;  // no -1 terminator up to this draft
+    for (int i = 0; i <= tid; ++i) listed = listed && (sh_ids[i] >= 0);
+    if (listed && !a.greedy) {
+      const int x = min(sh_ids[tid], a.V - 1);  // out-of-range ids are flagged
+      lp = (double)load1(row_ptr(a, b, tid), x, a.f32);
+      lq = (double)load1(row_ptr(a, b, N + tid), x, a.f32);
+    }
+  }
   // Row merge: thread rho walks its S1 slices in order.
   if (tid < R) {
-    const double2* st = a.stats + ((size_t)b * R + tid) * a.S1;
+    const double2* st = st_in_lds ? sh_st + tid * a.S1 : st_g + tid * a.S1;
     if (a.greedy) {
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
@@ -274,30 +304,23 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* out_plan, int* out_k
       sh_s[tid] = S;
     }
   }
-  if (tid < K) sh_ids[tid] = a.drafts[(size_t)b * K + tid];
   __syncthreads();
   // Per-draft inputs of the ratio test, one thread per draft.
-  if (tid < K) {
-    bool listed = true;  // no -1 terminator before this draft
-    for (int i = 0; i <= tid; ++i) listed = listed && (sh_ids[i] >= 0);
-    if (listed) {
-      const int x = min(sh_ids[tid], a.V - 1);  // out-of-range ids are flagged
-      const U64x4 w = philox4x64_10((uint64_t)tid, 0, 0, 0, a.seed, (uint64_t)b);
-      double p, q;
-      if (a.greedy) {
-        p = (x == (int)sh_s[tid]) ? 1.0 : 0.0;
-        q = (x == (int)sh_s[N + tid]) ? 1.0 : 0.0;
-      } else {
-        const double lp = (double)load1(row_ptr(a, b, tid), x, a.f32);
-        const double lq = (double)load1(row_ptr(a, b, N + tid), x, a.f32);
-        p = exp((lp - sh_m[tid]) * a.invT) / sh_s[tid];
-        q = exp((lq - sh_m[N + tid]) * a.invT) / sh_s[N + tid];
-      }
-      sh_draft[tid][0] = p;
-      sh_draft[tid][1] = q;
-      sh_draft[tid][2] = top24(w.w[0]);
-      sh_draft[tid][3] = top24(w.w[1]);
+  if (tid < K && listed) {
+    const int x = min(sh_ids[tid], a.V - 1);
+    const U64x4 w = philox4x64_10((uint64_t)tid, 0, 0, 0, a.seed, (uint64_t)b);
+    double p, q;
+    if (a.greedy) {
+      p = (x == (int)sh_s[tid]) ? 1.0 : 0.0;
+      q = (x == (int)sh_s[N + tid]) ? 1.0 : 0.0;
+    } else {
+      p = exp((lp - sh_m[tid]) * a.invT) / sh_s[tid];
+      q = exp((lq - sh_m[N + tid]) * a.invT) / sh_s[N + tid];
     }
+    sh_draft[tid][0] = p;
+    sh_draft[tid][1] = q;
+    sh_draft[tid][2] = top24(w.w[0]);
+    sh_draft[tid][3] = top24(w.w[1]);
   }
   __syncthreads();
   if (tid == 0) {
@@ -403,12 +426,13 @@ __device__ inline double subchunk_scan(const AccArgs& a, const SamplePlan& sp, i
 }
 
 // This thread's 8 logits of sub-chunk sc in the p row (and q row, mode 0).
+template <bool VEC, bool F32>
 __device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, int mode, int sc,
                                 float xp[8], float xq[8]) {
   const int v = sc * kSub + 8 * threadIdx.x;
-  load8(row_ptr(a, b, sp.row_p), v, a.V, a.f32, a.vec_ok, xp);
+  load8<VEC, F32>(row_ptr(a, b, sp.row_p), v, a.V, xp);
   if (mode == 0) {
-    load8(row_ptr(a, b, a.N + sp.row_q), v, a.V, a.f32, a.vec_ok, xq);
+    load8<VEC, F32>(row_ptr(a, b, a.N + sp.row_q), v, a.V, xq);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) xq[e] = -INFINITY;
@@ -417,7 +441,9 @@ __device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, i
 
 constexpr int kMaxSpw = 4;  // upper bound of AcceptPlan::spw
 
+template <bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
+  __shared__ double2 sh_st[kDecideStats];
   __shared__ double sh_draft[16][4];
   __shared__ double sh_m[32], sh_s[32];
   __shared__ int sh_ids[16];
@@ -427,7 +453,7 @@ __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
   const int tid = threadIdx.x;
   const int b = (int)(blockIdx.x / a.S2);
   const int w0 = (int)(blockIdx.x % a.S2);
-  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_m, sh_s, sh_ids);
+  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_m, sh_s, sh_ids, sh_st);
   const SamplePlan sp = sh_plan;
   if (w0 == 0) {
     write_prefix(a, b, sp, sh_kp, sh_draft, sh_ids);
@@ -439,7 +465,7 @@ __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
   float xp[kMaxSpw][8], xq[kMaxSpw][8];
 #pragma unroll
   for (int k = 0; k < kMaxSpw; ++k)
-    if (sc_lo + k < sc_hi) load_sub(a, b, sp, sp.mode, sc_lo + k, xp[k], xq[k]);
+    if (sc_lo + k < sc_hi) load_sub<VEC, F32>(a, b, sp, sp.mode, sc_lo + k, xp[k], xq[k]);
   double w[8];
   double* subs = a.subsum + (size_t)b * a.nsub;
 #pragma unroll
@@ -453,6 +479,7 @@ __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
 // ---------------------------------------------------------------------------
 // Kernel 3: locate t and scan one sub-chunk.
 // ---------------------------------------------------------------------------
+template <bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   __shared__ double sh_wave[4], sh_incl[256];
   __shared__ double sh_sub[kMaxSubChunks];
@@ -461,13 +488,12 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   __shared__ int found_tok, found_last;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  const double* subs = a.subsum + (size_t)b * a.nsub;
+  for (int i = tid; i < a.nsub; i += 256) sh_sub[i] = subs[i];
   const SamplePlan sp = a.plan[b];
   if (sp.mode == 2) return;
-  const double* subs = a.subsum + (size_t)b * a.nsub;
   float xp[8], xq[8];
   double w[8];
-
-  for (int i = tid; i < a.nsub; i += 256) sh_sub[i] = subs[i];
   __syncthreads();
   if (tid == 0) {
     double W = 0.0;
@@ -479,7 +505,7 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   if (!(sh_W > 0.0)) {
     // The residual vanished to rounding: fall back to p_j over the whole row.
     for (int sc = 0; sc < a.nsub; ++sc) {
-      load_sub(a, b, sp, 1, sc, xp, xq);
+      load_sub<VEC, F32>(a, b, sp, 1, sc, xp, xq);
       const double tot = subchunk_scan(a, sp, 1, xp, xq, w, sh_wave, sh_incl);
       if (tid == 0) sh_sub[sc] = tot;
     }
@@ -516,7 +542,7 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   __syncthreads();
   const double t = sh_t, base = sh_base;
   const int sc = sh_sc, mode = sh_mode;
-  load_sub(a, b, sp, mode, sc, xp, xq);
+  load_sub<VEC, F32>(a, b, sp, mode, sc, xp, xq);
   subchunk_scan(a, sp, mode, xp, xq, w, sh_wave, sh_incl);
   const int v0 = sc * kSub + 8 * tid;
   int lastp = -1;
@@ -558,10 +584,30 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   }
 }
 
-template <int U>
+template <int U, bool VEC, bool F32>
 int32_t launch_stats(const AccArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)a.B * a.R * a.S1;
-  hipLaunchKernelGGL((accept_stats_kernel<U>), dim3((unsigned)g), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((accept_stats_kernel<U, VEC, F32>), dim3((unsigned)g), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
+}
+
+template <bool VEC, bool F32>
+int32_t launch_all(AccArgs a, int U1, hipStream_t s) {
+  int32_t r;
+  switch (U1) {
+    case 8: r = launch_stats<8, VEC, F32>(a, s); break;
+    case 4: r = launch_stats<4, VEC, F32>(a, s); break;
+    case 2: r = launch_stats<2, VEC, F32>(a, s); break;
+    default: r = launch_stats<1, VEC, F32>(a, s); break;
+  }
+  if (r != IDLM_OK) return r;
+  // Greedy needs one decision work-group per sequence and no sampling.
+  if (a.greedy) a.S2 = 1;
+  const int64_t g2 = (int64_t)a.B * a.S2;
+  hipLaunchKernelGGL((accept_decide_sum_kernel<VEC, F32>), dim3((unsigned)g2), dim3(256), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
+  if (a.greedy) return IDLM_OK;
+  hipLaunchKernelGGL((accept_select_kernel<VEC, F32>), dim3((unsigned)a.B), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
@@ -597,25 +643,10 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.spw = ap.spw;
   a.S2 = ap.S2;
   a.f32 = d.logits_dtype == IDLM_F32;
-  const size_t es = a.f32 ? 4 : 2;
-  a.vec_ok = ((size_t)d.V * es) % 16 == 0 && ((uintptr_t)lc % 16) == 0 &&
-             (lm == nullptr || ((uintptr_t)lm % 16) == 0);
-  int32_t r;
-  switch (ap.U1) {
-    case 8: r = launch_stats<8>(a, s); break;
-    case 4: r = launch_stats<4>(a, s); break;
-    case 2: r = launch_stats<2>(a, s); break;
-    default: r = launch_stats<1>(a, s); break;
-  }
-  if (r != IDLM_OK) return r;
-  // Greedy needs one decision work-group per sequence and no sampling.
-  if (a.greedy) a.S2 = 1;
-  const int64_t g2 = (int64_t)d.B * a.S2;
-  hipLaunchKernelGGL(accept_decide_sum_kernel, dim3((unsigned)g2), dim3(256), 0, s, a);
-  if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
-  if (a.greedy) return IDLM_OK;
-  hipLaunchKernelGGL(accept_select_kernel, dim3((unsigned)d.B), dim3(256), 0, s, a);
-  return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
+  const bool vec = d.V % 8 == 0 && ((uintptr_t)lc % 16) == 0 &&
+                   (lm == nullptr || ((uintptr_t)lm % 16) == 0);
+  if (a.f32) return vec ? launch_all<true, true>(a, ap.U1, s) : launch_all<false, true>(a, ap.U1, s);
+  return vec ? launch_all<true, false>(a, ap.U1, s) : launch_all<false, false>(a, ap.U1, s);
 }
 
 }  // namespace idlm

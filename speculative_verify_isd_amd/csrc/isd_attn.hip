@@ -433,8 +433,11 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
 template <int D, int WR>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * WR;
+  constexpr int kMergeVec = (ROWS * D / 4 + 255) / 256;  // float4 outputs per thread
+  constexpr int kMergeBlock = 16;                         // pieces per LDS block
   __shared__ int64_t sh_sum[4][2];
   __shared__ float sh_M[ROWS], sh_iL[ROWS];
+  __shared__ float sh_f[kMergeBlock][ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pair = blockIdx.x;
   const int b = pair / a.Hkv, h = pair % a.Hkv;
@@ -469,11 +472,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int npieces = wb - wa + 1;
   const int slot0 = (start == (int64_t)wa * span) ? 0 : 1;
   auto slot_of = [&](int k) { return (size_t)(wa + k) * 2 + (k == 0 ? slot0 : 0); };
-  if (tid < ROWS) {
+  // Row maxima and normalisers over all pieces (independent loads, 4 at a time).
+  if (tid < a.RG) {
     float M = -INFINITY;
+#pragma unroll 4
     for (int k = 0; k < npieces; ++k) M = fmaxf(M, a.part_ml[slot_of(k) * ROWS + tid].x);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float L = 0.f;
+#pragma unroll 4
     for (int k = 0; k < npieces; ++k) {
       const float2 ml = a.part_ml[slot_of(k) * ROWS + tid];
       L += ml.y * exp2f(ml.x - Mu);
@@ -482,18 +488,49 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     sh_iL[tid] = 1.f / L;
   }
   __syncthreads();
-  u16* outp = (u16*)a.out;
-  for (int idx = tid; idx < a.RG * D; idx += 256) {
-    const int row = idx / D, d = idx % D;
-    const float Mu = sh_M[row];
-    float O = 0.f;
-    for (int k = 0; k < npieces; ++k) {
-      const size_t s = slot_of(k);
-      O += a.part_o[(s * ROWS + row) * D + d] * exp2f(a.part_ml[s * ROWS + row].x - Mu);
+  // Each thread owns up to kMergeVec 4-wide d groups of the R*G x D output;
+  // pieces are folded in blocks whose scale factors sit in LDS.
+  constexpr int D4 = D / 4;
+  const int nvec = a.RG * D4;
+  float4 O[kMergeVec];
+#pragma unroll
+  for (int e = 0; e < kMergeVec; ++e) O[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int kb = 0; kb < npieces; kb += kMergeBlock) {
+    const int nk = min(kMergeBlock, npieces - kb);
+    for (int i = tid; i < nk * a.RG; i += 256) {
+      const int k = kb + i / a.RG, row = i % a.RG;
+      sh_f[i / a.RG][row] = exp2f(a.part_ml[slot_of(k) * ROWS + row].x - sh_M[row]) * sh_iL[row];
     }
-    const int r = row / a.G, g = row % a.G;
-    outp[(((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D + d] =
-        f32_to_bf16_rne(O * sh_iL[row]);
+    __syncthreads();
+    for (int k = 0; k < nk; ++k) {
+      const float4* po = (const float4*)(a.part_o + slot_of(kb + k) * ROWS * D);
+#pragma unroll
+      for (int e = 0; e < kMergeVec; ++e) {
+        const int i = tid + 256 * e;
+        if (i < nvec) {
+          const float4 v = po[(i / D4) * D4 + i % D4];
+          const float f = sh_f[k][i / D4];
+          O[e].x += v.x * f;
+          O[e].y += v.y * f;
+          O[e].z += v.z * f;
+          O[e].w += v.w * f;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  u16* outp = (u16*)a.out;
+#pragma unroll
+  for (int e = 0; e < kMergeVec; ++e) {
+    const int i = tid + 256 * e;
+    if (i < nvec) {
+      const int row = i / D4, d = 4 * (i % D4);
+      const int r = row / a.G, g = row % a.G;
+      const unsigned lo = f32_to_bf16_rne(O[e].x) | ((unsigned)f32_to_bf16_rne(O[e].y) << 16);
+      const unsigned hi = f32_to_bf16_rne(O[e].z) | ((unsigned)f32_to_bf16_rne(O[e].w) << 16);
+      *(uint2*)(outp + (((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D + d) =
+          make_uint2(lo, hi);
+    }
   }
 }
 

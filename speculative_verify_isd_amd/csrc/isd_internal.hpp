@@ -13,6 +13,7 @@ namespace idlm {
 constexpr int kPage = 16;
 constexpr int kSub = 2048;  // acceptance sub-chunk: 256 threads x 8 elements
 constexpr int kMaxSubChunks = 1024;  // V <= kSub * kMaxSubChunks
+constexpr int kDecideStats = 1024;   // slice statistics a decision stages in LDS
 constexpr int kMaxWaves = 2048;   // streaming-attention waves resident at once (upper bound)
 constexpr int kMinRunPages = 8;   // shortest run of pages given to one wave-lane
 
