@@ -9,26 +9,27 @@
 // guarantee holds) and the committed prefix ends there; with every draft
 // kept, the last clean row supplies a bonus token.
 //
-// Three launches; kernel boundaries are the only synchronisation (no
+// Four launches; kernel boundaries are the only synchronisation (no
 // atomics, no fences), and every reduction runs in a fixed order, so results
 // do not depend on scheduling:
 //
-//   accept_stats       grid B*R*S1.  Each work-group reduces one slice of one
-//                      logit row to (raw max m, sum of exp2((l - m) c)) with
-//                      c = log2(e)/T: every load of the slice is issued before
-//                      any arithmetic, exponentials in float32, sums in
-//                      float64.  Greedy (T = 0): (max, lowest argmax).
-//   accept_decide_sum  grid B*S2.  Each work-group recomputes its sequence's
-//                      decision from the slice statistics (row merge, p_i(x_i)
-//                      and q_i(x_i) in float64, Philox uniforms, sequential
-//                      ratio test), then sums the sampling weights (residual
-//                      max(0, p_j - q_j) or bonus p) of its 2048-element
-//                      sub-chunks.  Its first work-group writes the kept
-//                      prefix, the accept length and the plan.
-//   accept_select      grid B.  Prefixes the sub-chunk sums in order, finds
-//                      the sub-chunk holding t = u' * sum(w), recomputes it
-//                      bit for bit and scans it to the smallest v whose
-//                      running sum exceeds t.
+//   accept_stats   grid B*R*S1.  Each work-group reduces one slice of one
+//                  logit row to (max m, sum of exp2((l - m) c)) with
+//                  c = log2(e)/T: every load of the slice is issued before any
+//                  arithmetic, the slice max is reduced first so each element
+//                  costs one float32 exponential, sums are float64.  Greedy
+//                  (T = 0): (max, lowest argmax).
+//   accept_decide  grid B.  Merges the slices of each row in order, evaluates
+//                  p_i(x_i) and q_i(x_i) in float64, draws the Philox
+//                  uniforms, runs the sequential ratio test and writes the
+//                  kept prefix, the accept length and the sampling plan (the
+//                  whole answer when T = 0).
+//   accept_sum     grid B*S2.  Sums the sampling weights (residual
+//                  max(0, p_j - q_j) or bonus p) of 2048-element sub-chunks.
+//   accept_select  grid B.  Prefixes the sub-chunk sums in order, finds the
+//                  sub-chunk holding t = u' * sum(w), recomputes it bit for
+//                  bit and scans it to the smallest v whose running sum
+//                  exceeds t.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -208,43 +209,34 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
     for (int w = 1; w < 4; ++w) better(bv, bi, sh_m[w], sh_i[w]);
     res = make_double2((double)bv, (double)bi);
   } else {
+    // Slice max first (float32), then one exponential per element relative
+    // to it, so the sums need no rescaling.
     float m = -INFINITY;
 #pragma unroll
     for (int k = 0; k < U; ++k)
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, x[k][e]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) sh_m[wave] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
     double s = 0.0;
-    if (m != -INFINITY) {
+    if (M != -INFINITY) {
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part += exp2f((x[k][e] - m) * a.c2);
+        for (int e = 0; e < 8; ++e) part += __builtin_amdgcn_exp2f((x[k][e] - M) * a.c2);
         s += (double)part;
       }
     }
-    // Work-group merge; m is a raw logit, so rescale with the same c2.
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float mo = __shfl_xor(m, off);
-      const double so = __shfl_xor(s, off);
-      const float M = fmaxf(m, mo);
-      if (M != -INFINITY)
-        s = (m == -INFINITY ? 0.0 : s * exp2((double)(m - M) * a.c2)) +
-            (mo == -INFINITY ? 0.0 : so * exp2((double)(mo - M) * a.c2));
-      m = M;
-    }
-    if (lane == 0) {
-      sh_m[wave] = m;
-      sh_s[wave] = s;
-    }
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) sh_s[wave] = s;
     __syncthreads();
     if (tid != 0) return;
-    const float M = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
-    double S = 0.0;
-    for (int w = 0; w < 4; ++w)
-      if (sh_m[w] != -INFINITY) S += sh_s[w] * exp2((double)(sh_m[w] - M) * a.c2);
-    res = make_double2((double)M, S);
+    res = make_double2((double)M, ((sh_s[0] + sh_s[1]) + sh_s[2]) + sh_s[3]);
   }
   a.stats[((size_t)b * a.R + rho) * a.S1 + c] = res;
 }
@@ -404,10 +396,11 @@ __device__ inline void weights8(const AccArgs& a, const SamplePlan& sp, int mode
     const double iq = 1.0 / sp.sq;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      w[e] = fmax(0.0, (double)exp2f((xp[e] - mp) * c2) * ip - (double)exp2f((xq[e] - mq) * c2) * iq);
+      w[e] = fmax(0.0, (double)__builtin_amdgcn_exp2f((xp[e] - mp) * c2) * ip -
+                           (double)__builtin_amdgcn_exp2f((xq[e] - mq) * c2) * iq);
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = (double)exp2f((xp[e] - mp) * c2) * ip;
+    for (int e = 0; e < 8; ++e) w[e] = (double)__builtin_amdgcn_exp2f((xp[e] - mp) * c2) * ip;
   }
 }
 
@@ -441,36 +434,40 @@ __device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, i
 
 constexpr int kMaxSpw = 4;  // upper bound of AcceptPlan::spw
 
-template <bool VEC, bool F32>
-__global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
+// One work-group per sequence: the decision, the kept prefix and the plan.
+__global__ __launch_bounds__(256) void accept_decide_kernel(AccArgs a) {
   __shared__ double2 sh_st[kDecideStats];
   __shared__ double sh_draft[16][4];
   __shared__ double sh_m[32], sh_s[32];
   __shared__ int sh_ids[16];
   __shared__ SamplePlan sh_plan;
   __shared__ int sh_kp;
+  const int b = blockIdx.x;
+  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_m, sh_s, sh_ids, sh_st);
+  write_prefix(a, b, sh_plan, sh_kp, sh_draft, sh_ids);
+  if (threadIdx.x == 0) a.plan[b] = sh_plan;
+}
+
+// Sub-chunk sums of the sampling weights: every load of the work-group's
+// sub-chunks is issued right after the plan arrives.
+template <bool VEC, bool F32>
+__global__ __launch_bounds__(256) void accept_sum_kernel(AccArgs a) {
   __shared__ double sh_wave[4], sh_incl[256];
   const int tid = threadIdx.x;
   const int b = (int)(blockIdx.x / a.S2);
   const int w0 = (int)(blockIdx.x % a.S2);
-  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_m, sh_s, sh_ids, sh_st);
-  const SamplePlan sp = sh_plan;
-  if (w0 == 0) {
-    write_prefix(a, b, sp, sh_kp, sh_draft, sh_ids);
-    if (tid == 0) a.plan[b] = sp;
-  }
+  const SamplePlan sp = a.plan[b];
   if (sp.mode == 2) return;  // greedy: nothing to sample
-
-  const int sc_lo = w0 * a.spw, sc_hi = min(a.nsub, sc_lo + a.spw);
+  const int sc_lo = w0 * a.spw, n = min(a.nsub - sc_lo, a.spw);
   float xp[kMaxSpw][8], xq[kMaxSpw][8];
 #pragma unroll
-  for (int k = 0; k < kMaxSpw; ++k)
-    if (sc_lo + k < sc_hi) load_sub<VEC, F32>(a, b, sp, sp.mode, sc_lo + k, xp[k], xq[k]);
+  for (int k = 0; k < kMaxSpw; ++k)  // clamped, unconditional: all loads in flight together
+    load_sub<VEC, F32>(a, b, sp, sp.mode, sc_lo + min(k, n - 1), xp[k], xq[k]);
   double w[8];
   double* subs = a.subsum + (size_t)b * a.nsub;
 #pragma unroll
   for (int k = 0; k < kMaxSpw; ++k)
-    if (sc_lo + k < sc_hi) {
+    if (k < n) {
       const double tot = subchunk_scan(a, sp, sp.mode, xp[k], xq[k], w, sh_wave, sh_incl);
       if (tid == 0) subs[sc_lo + k] = tot;
     }
@@ -601,12 +598,12 @@ int32_t launch_all(AccArgs a, int U1, hipStream_t s) {
     default: r = launch_stats<1, VEC, F32>(a, s); break;
   }
   if (r != IDLM_OK) return r;
-  // Greedy needs one decision work-group per sequence and no sampling.
-  if (a.greedy) a.S2 = 1;
-  const int64_t g2 = (int64_t)a.B * a.S2;
-  hipLaunchKernelGGL((accept_decide_sum_kernel<VEC, F32>), dim3((unsigned)g2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(accept_decide_kernel, dim3((unsigned)a.B), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
-  if (a.greedy) return IDLM_OK;
+  if (a.greedy) return IDLM_OK;  // the decision already wrote the argmax tokens
+  const int64_t g2 = (int64_t)a.B * a.S2;
+  hipLaunchKernelGGL((accept_sum_kernel<VEC, F32>), dim3((unsigned)g2), dim3(256), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
   hipLaunchKernelGGL((accept_select_kernel<VEC, F32>), dim3((unsigned)a.B), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
