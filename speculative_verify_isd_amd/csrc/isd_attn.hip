@@ -25,19 +25,20 @@
 //   WR = 2 or 4 waves of a work-group walk the same run, one 32-row group
 //   each; otherwise the 4 waves are 4 independent lanes.
 //
-//   Per two pages (32 tokens) and 16-row block a wave runs
+//   Per page (16 tokens) and 16-row block a wave runs
 //     S^T[tok][row] = K[tok][:] . Q[row][:]   (D/32 x mfma_f32_16x16x32_bf16)
 //     online softmax on S^T (rows in lanes, tokens in registers)
-//     O^T[d][row]  += V^T[d][tok] . P^T[tok][row]  (D/16 x 16x16x32)
+//     O^T[d][row]  += V^T[d][tok] . P^T[tok][row]  (D/16 x mfma_f32_16x16x16_bf16)
 //   The S^T accumulator layout is exactly the B-operand layout P^T needs,
 //   and O^T keeps rows in lanes, so the softmax needs no data movement
 //   beyond two row-swap permutes for the max.
 //
 //   The page layout is chosen for these operands: each K fragment load is a
 //   contiguous 1 KiB per wave (16 B per lane) and each V^T fragment load a
-//   contiguous 512 B, so pages stream straight into VGPRs.  Two register
-//   buffers keep one step's loads in flight while the previous step
-//   computes; page ids are wave-uniform loads.
+//   contiguous 512 B, so pages stream straight into VGPRs.  A ring of page
+//   buffers keeps several pages' loads in flight while one page computes
+//   (the query fragments live in LDS to leave registers to the ring); page
+//   ids are wave-uniform loads.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -47,6 +48,9 @@ namespace idlm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 
@@ -85,36 +89,48 @@ __device__ inline int clamp_ctx(const AttnArgs& a, int ctx, bool report) {
 
 __device__ inline int pages_of(int ctx) { return (ctx + kPage - 1) / kPage; }
 
+// Read-only loads of wave-uniform addresses through the constant address
+// space, so they are scalar-cache loads (counted apart from the vector
+// loads the K/V pipeline waits on).
+typedef const int32_t __attribute__((address_space(4)))* cint_ptr;
+__device__ inline int sload(const int32_t* p, size_t i) { return ((cint_ptr)p)[i]; }
+
+// Marks a wave-uniform value as such, so address arithmetic built from it
+// stays scalar and its loads go through the scalar cache.
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline int64_t uni64(int64_t x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(uint64_t)x);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA building blocks
 // ---------------------------------------------------------------------------
 
-// K and V^T fragments of two consecutive pages for one wave.
+// K and V^T fragments of one page for one wave (32 registers).
 template <int D>
-struct KVFrag {
-  bf16x8 k[2][D / 32];
-  bf16x8 v[D / 16];  // page a's 4 tokens, then page b's 4 tokens
+struct PageFrag {
+  bf16x8 k[D / 32];  // A operand of S^T = K Q^T: token lane%16, d chunk 4c + lane/16
+  s16x4 v[D / 16];   // A operand of O^T += V^T P^T: d = 16j + lane%16, tokens 4(lane/16)+0..3
 };
 
-// Issue the loads of one two-page step.  K: one contiguous 1 KiB per 32-wide
-// d step (16 B per lane); V^T: one contiguous 512 B per 16-wide d block.
+// Issue one page's loads.  K: one contiguous 1 KiB per 32-wide d step (16 B
+// per lane); V^T: one contiguous 512 B per 16-wide d block (8 B per lane).
+// Every KV byte is read once per step, so the loads are non-temporal: on
+// gfx950 that streams them past the caches and sustains ~13% more HBM
+// bandwidth than ordinary loads.
 template <int D>
-__device__ inline void load_step(KVFrag<D>& f, const u16* kva, const u16* kvb, size_t v_off,
-                                 int lane) {
+__device__ inline void load_page(PageFrag<D>& f, const u16* kv, size_t v_off, int lane) {
   constexpr int NC = D / 32, ND = D / 16;
   const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    f.k[0][c] = __builtin_bit_cast(bf16x8, *(const uint4*)(kva + 512 * c + 8 * lane));
-    f.k[1][c] = __builtin_bit_cast(bf16x8, *(const uint4*)(kvb + 512 * c + 8 * lane));
-  }
+  for (int c = 0; c < NC; ++c)
+    f.k[c] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(kv + 512 * c + 8 * lane)));
 #pragma unroll
-  for (int j = 0; j < ND; ++j) {
-    const size_t o = v_off + (size_t)(16 * j + col) * kPage + 4 * grp;
-    const uint2 va = *(const uint2*)(kva + o);
-    const uint2 vb = *(const uint2*)(kvb + o);
-    f.v[j] = __builtin_bit_cast(bf16x8, make_uint4(va.x, va.y, vb.x, vb.y));
-  }
+  for (int j = 0; j < ND; ++j)
+    f.v[j] = __builtin_bit_cast(
+        s16x4, __builtin_nontemporal_load((const u32x2*)(kv + v_off + (size_t)(16 * j + col) * kPage + 4 * grp)));
 }
 
 // Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with
@@ -134,41 +150,39 @@ __device__ inline float max_over_rows(float v) {
 // The final normalisation uses the same running max, so this is exact.
 constexpr float kLazyTau = 8.0f;
 
-// One two-page step for this wave's two 16-row blocks: S^T = K Q^T, online
-// softmax in exp2 space, O^T += V^T P^T.  MASKED applies the causal mask and
-// a missing second page; most steps are fully visible and skip it.
+// One page (16 tokens) for this wave's two 16-row blocks: S^T = K Q^T
+// (mfma 16x16x32), online softmax in exp2 space, O^T += V^T P^T (mfma
+// 16x16x16: the S^T accumulator is already P^T's B-operand layout).  MASKED
+// applies the causal mask (and masks a padding step entirely when !has).
 template <int D, bool MASKED>
-__device__ inline void compute_step(const KVFrag<D>& f, const bf16x8 (&qf)[2][D / 32],
-                                    const int (&pos)[2], int ta, bool hasa, bool hasb,
-                                    float c2, float (&m)[2], float (&l)[2],
-                                    f32x4 (&acc)[2][D / 16]) {
+__device__ inline void compute_page(const PageFrag<D>& f, const bf16x8* qs, int lane,
+                                    const int (&pos)[2], int t, bool has, float c2,
+                                    float (&m)[2], float (&l)[2], f32x4 (&acc)[2][D / 16]) {
   constexpr int NC = D / 32, ND = D / 16;
-  f32x4 sc[2][2];
+  // Query fragments come from this wave's LDS copy (registers are kept for
+  // the K/V pipeline).
+  bf16x8 qf[2][NC];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg) sc[rb][pg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c) qf[rb][c] = qs[(rb * NC + c) * 64 + lane];
+  f32x4 sc[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) sc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int pg = 0; pg < 2; ++pg)
-        sc[rb][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[pg][c], qf[rb][c], sc[rb][pg], 0, 0, 0);
+      sc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[c], qf[rb][c], sc[rb], 0, 0, 0);
 
   float mx[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     if (MASKED) {
-      const int tb = ta + kPage;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sc[rb][0][e] = (hasa && ta + e <= pos[rb]) ? sc[rb][0][e] : -INFINITY;
-        sc[rb][1][e] = (hasb && tb + e <= pos[rb]) ? sc[rb][1][e] : -INFINITY;
-      }
+      for (int e = 0; e < 4; ++e) sc[rb][e] = (has && t + e <= pos[rb]) ? sc[rb][e] : -INFINITY;
     }
-    float v = fmaxf(fmaxf(sc[rb][0][0], sc[rb][0][1]), fmaxf(sc[rb][0][2], sc[rb][0][3]));
-    v = fmaxf(v, fmaxf(fmaxf(sc[rb][1][0], sc[rb][1][1]), fmaxf(sc[rb][1][2], sc[rb][1][3])));
+    const float v = fmaxf(fmaxf(sc[rb][0], sc[rb][1]), fmaxf(sc[rb][2], sc[rb][3]));
     mx[rb] = max_over_rows(v) * c2;
   }
   if (__any((mx[0] > m[0] + kLazyTau) || (mx[1] > m[1] + kLazyTau))) {
@@ -185,20 +199,16 @@ __device__ inline void compute_step(const KVFrag<D>& f, const bf16x8 (&qf)[2][D 
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const float mneg = (m[rb] == -INFINITY) ? 0.f : -m[rb];
-    bf16x8 pf;
-    float ps = 0.f;
+    float p[4];
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[rb][pg][e], c2, mneg));
-        ps += p;
-        pf[4 * pg + e] = (__bf16)p;
-      }
-    l[rb] += ps;
+    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[rb][e], c2, mneg));
+    l[rb] += (p[0] + p[1]) + (p[2] + p[3]);
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+    const s16x4 pf = __builtin_bit_cast(s16x4, pb);
 #pragma unroll
     for (int j = 0; j < ND; ++j)
-      acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v[j], pf, acc[rb][j], 0, 0, 0);
+      acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(f.v[j], pf, acc[rb][j], 0, 0, 0);
   }
 }
 
@@ -256,22 +266,26 @@ __device__ inline int64_t run_length(int64_t total, int nlanes) {
 // ---------------------------------------------------------------------------
 template <int D, int WR>
 __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
+  constexpr int kRing = D == 128 ? kRingPages : kRingPages + 2;  // page buffers per wave
   constexpr int NC = D / 32;  // K-dim steps of the QK product
   constexpr int ND = D / 16;  // 16-wide d blocks of the PV product
   constexpr int WK = 4 / WR;  // independent lanes per work-group
   constexpr int ROWS = 32 * WR;
 
+  __shared__ bf16x8 lds_q[4][2 * NC * 64];  // each wave's query fragments
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rgrp = wave % WR;
   const int wl = blockIdx.x * WK + wave / WR;  // this wave-lane
+  bf16x8* qs = lds_q[wave];
   const int col = lane & 15, grp = lane >> 4;
 
   // Bad contexts are flagged once, by the first wave of the grid.
   if (blockIdx.x == 0 && wave == 0)
     for (int b = lane; b < a.B; b += 64) clamp_ctx(a, a.ctx_lens[b], true);
 
-  const int64_t total = total_units_wave(a);
+  const int64_t total = uni64(total_units_wave(a));
   const int64_t span = run_length(total, a.nlanes);
   int64_t u = (int64_t)wl * span;
   const int64_t uend = min(u + span, total);
@@ -280,6 +294,9 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
   int64_t ub;
   int ctx;
   int b = locate_seq(a, u, &ub, &ctx);
+  b = uni(b);
+  ub = uni64(ub);
+  ctx = uni(ctx);
   int np = pages_of(ctx);
   int h = (int)((u - ub) / np);
 
@@ -300,8 +317,8 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
     const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
 
     // Query fragments (B operand of S^T = K Q^T): row = lane's column, eight
-    // consecutive d per lane; k-step c covers d chunk 4c + grp.
-    bf16x8 qf[2][NC];
+    // consecutive d per lane; k-step c covers d chunk 4c + grp.  Staged in
+    // this wave's LDS slot; a wave's own LDS accesses stay in order.
     int pos[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -312,9 +329,10 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
       pos[rb] = ctx - a.R + r;
       const u16* qp = qb + (((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const uint4 v = valid ? *(const uint4*)(qp + 8 * (4 * c + grp)) : make_uint4(0, 0, 0, 0);
-        qf[rb][c] = __builtin_bit_cast(bf16x8, v);
+      for (int c = 0; c < NC; ++c) {  // padding rows load a real row, then zero it
+        uint4 v = *(const uint4*)(qp + 8 * (4 * c + grp));
+        if (!valid) v = make_uint4(0, 0, 0, 0);
+        qs[(rb * NC + c) * 64 + lane] = __builtin_bit_cast(bf16x8, v);
       }
     }
     float m[2] = {-INFINITY, -INFINITY};
@@ -325,51 +343,43 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < ND; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Two-page steps.  Every prefetch is issued unconditionally (so the
-    // compiler waits for exactly one buffer at a time); a prefetch past the
-    // end re-reads the last step (a cache hit) and its compute is masked.
-    // The scheduling barriers keep each prefetch ahead of the compute it
-    // must overlap.
-    const int nsteps = (nseg + 1) / 2;
-    const int last = nsteps - 1;
-    const int nrun = nsteps + (nsteps & 1);
+    // One page per step through a ring of kRing register buffers: kRing-1
+    // pages are in flight while one computes.  Every prefetch is issued
+    // unconditionally (so the compiler waits for exactly one buffer at a
+    // time); prefetches past the end re-read the last page (a cache hit) and
+    // their compute is fully masked.  The scheduling barriers keep each
+    // prefetch ahead of the compute it must overlap.
+    const int last = nseg - 1;
+    const int nrun = ((nseg + kRing - 1) / kRing) * kRing;
     const int minpos = ctx - a.R;  // every row sees tokens up to here
-    auto page_id = [&](int p) {
-      int id = pt[p];
+    auto issue = [&](PageFrag<D>& f, int st) {
+      const int pg = p0 + min(st, last);
+      int id = sload(pt, pg);
       if ((unsigned)id >= (unsigned)a.num_pages) {
         flag(a.status, kBadPage);
         id = 0;
       }
-      return id;
+      load_page<D>(f, kvb + (size_t)id * page_elems + head_off, v_off, lane);
     };
-    auto issue = [&](KVFrag<D>& f, int st) {
-      const int pa = p0 + 2 * min(st, last);
-      const int ida = page_id(pa);
-      const int idb = pa + 1 < p1 ? page_id(pa + 1) : ida;
-      load_step<D>(f, kvb + (size_t)ida * page_elems + head_off,
-                   kvb + (size_t)idb * page_elems + head_off, v_off, lane);
-    };
-    auto run = [&](const KVFrag<D>& f, int st) {
-      const int pa = p0 + 2 * st;
-      const bool valid = st < nsteps;
-      const bool hasb = valid && pa + 1 < p1;
-      const int t0 = pa * kPage;
-      if (hasb && t0 + 2 * kPage - 1 <= minpos)
-        compute_step<D, false>(f, qf, pos, t0 + 4 * grp, true, true, a.scale_log2, m, l, acc);
+    auto run = [&](const PageFrag<D>& f, int st) {
+      const int t0 = (p0 + st) * kPage;
+      const bool has = st < nseg;
+      if (has && t0 + kPage - 1 <= minpos)
+        compute_page<D, false>(f, qs, lane, pos, t0 + 4 * grp, true, a.scale_log2, m, l, acc);
       else
-        compute_step<D, true>(f, qf, pos, t0 + 4 * grp, valid, hasb, a.scale_log2, m, l, acc);
+        compute_page<D, true>(f, qs, lane, pos, t0 + 4 * grp, has, a.scale_log2, m, l, acc);
     };
-    KVFrag<D> f0, f1;
-    issue(f0, 0);
-    for (int st = 0; st < nrun; st += 2) {
-      issue(f1, st + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      run(f0, st);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(f0, st + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      run(f1, st + 1);
-      __builtin_amdgcn_sched_barrier(0);
+    PageFrag<D> ring[kRing];
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i) issue(ring[i], i);
+    for (int st = 0; st < nrun; st += kRing) {
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) {
+        issue(ring[(i + kRing - 1) % kRing], st + i + kRing - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        run(ring[i], st + i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // Row sums: every lane holds a partial over its tokens.
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
         h = 0;
         ub += (int64_t)np * a.Hkv;
         ++b;
-        ctx = clamp_ctx(a, a.ctx_lens[b], false);
+        ctx = uni(clamp_ctx(a, sload(a.ctx_lens, b), false));
         np = pages_of(ctx);
       }
     }

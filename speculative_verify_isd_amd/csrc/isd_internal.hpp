@@ -8,6 +8,10 @@
 
 #include "../../include/idlm_isd.h"
 
+#ifndef RING_PAGES_DEFAULT
+#define RING_PAGES_DEFAULT 2
+#endif
+
 namespace idlm {
 
 constexpr int kPage = 16;
@@ -16,6 +20,7 @@ constexpr int kMaxSubChunks = 1024;  // V <= kSub * kMaxSubChunks
 constexpr int kDecideStats = 1024;   // slice statistics a decision stages in LDS
 constexpr int kMaxWaves = 2048;   // streaming-attention waves resident at once (upper bound)
 constexpr int kMinRunPages = 8;   // shortest run of pages given to one wave-lane
+constexpr int kRingPages = RING_PAGES_DEFAULT;  // page buffers per attention wave (D = 128)
 
 // Sticky device status bits (workspace word 0).
 enum : int32_t { kBadPage = 1, kBadCtx = 2, kBadDraft = 4 };
