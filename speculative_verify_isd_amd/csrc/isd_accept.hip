@@ -9,27 +9,30 @@
 // guarantee holds) and the committed prefix ends there; with every draft
 // kept, the last clean row supplies a bonus token.
 //
-// Four launches; kernel boundaries are the only synchronisation (no
+// Three launches; kernel boundaries are the only synchronisation (no
 // atomics, no fences), and every reduction runs in a fixed order, so results
 // do not depend on scheduling:
 //
-//   accept_stats   grid B*R*S1.  Each work-group reduces one slice of one
-//                  logit row to (max m, sum of exp2((l - m) c)) with
-//                  c = log2(e)/T: every load of the slice is issued before any
-//                  arithmetic, the slice max is reduced first so each element
-//                  costs one float32 exponential, sums are float64.  Greedy
-//                  (T = 0): (max, lowest argmax).
-//   accept_decide  grid B.  Merges the slices of each row in order, evaluates
-//                  p_i(x_i) and q_i(x_i) in float64, draws the Philox
-//                  uniforms, runs the sequential ratio test and writes the
-//                  kept prefix, the accept length and the sampling plan (the
-//                  whole answer when T = 0).
-//   accept_sum     grid B*S2.  Sums the sampling weights (residual
-//                  max(0, p_j - q_j) or bonus p) of 2048-element sub-chunks.
-//   accept_select  grid B.  Prefixes the sub-chunk sums in order, finds the
-//                  sub-chunk holding t = u' * sum(w), recomputes it bit for
-//                  bit and scans it to the smallest v whose running sum
-//                  exceeds t.
+//   accept_stats       grid B*R*S1.  Each work-group reduces one slice of one
+//                      logit row to (max m, sum of exp2((l - m) c)) with
+//                      c = log2(e)/T: every load of the slice is issued before
+//                      any arithmetic, the slice max is reduced first so each
+//                      element costs one float32 exponential, sums are
+//                      float64.  The slice holding the row's draft also
+//                      records the draft's logit.  Greedy (T = 0): (max,
+//                      lowest argmax).
+//   accept_decide_sum  grid B*S2.  Every work-group of a sequence merges the
+//                      slices of each row in order, evaluates p_i(x_i) and
+//                      q_i(x_i) in float64, draws the Philox uniforms and runs
+//                      the sequential ratio test (one round of loads), then
+//                      sums the sampling weights (residual max(0, p_j - q_j)
+//                      or bonus p) of its 2048-element sub-chunks.  The first
+//                      work-group writes the kept prefix, the accept length
+//                      and the sampling plan (the whole answer when T = 0).
+//   accept_select      grid B.  Prefixes the sub-chunk sums in order, finds
+//                      the sub-chunk holding t = u' * sum(w), recomputes it
+//                      bit for bit and scans it to the smallest v whose
+//                      running sum exceeds t.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -87,6 +90,7 @@ struct AccArgs {
   double2* stats;   // [B][R][S1]: (m, s) or, greedy, (best value, best index)
   SamplePlan* plan; // [B]
   double* subsum;   // [B][nsub]
+  float* dlog;      // [B][R]: raw logit of the row's draft (rows that verify or proposed one)
   int B, N, K, R, V, S1, nsub, spw, S2, f32;
 };
 
@@ -141,20 +145,34 @@ __device__ inline void better(float& bv, int& bi, float v, int i) {
   }
 }
 
-// Inclusive scan of one double per thread over the work-group; every
-// thread's inclusive value lands in sh_incl[256].
-__device__ inline void wg_scan_incl(double x, double* sh_wave, double* sh_incl) {
+// Inclusive scans of NS doubles per thread over the work-group, run side by
+// side (one scan per index k, each in the same fixed order whatever NS is):
+// thread t's inclusive value for scan k lands in sh_incl[k][t].
+template <int NS>
+__device__ inline void wg_scan_incl(const double (&x0)[NS], double (*sh_wave)[4],
+                                    double (*sh_incl)[256]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double x[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) x[k] = x0[k];
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off);
-    if (lane >= off) x += y;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const double y = __shfl_up(x[k], off);
+      if (lane >= off) x[k] += y;
+    }
   }
-  if (lane == 63) sh_wave[wave] = x;
+  if (lane == 63)
+#pragma unroll
+    for (int k = 0; k < NS; ++k) sh_wave[k][wave] = x[k];
   __syncthreads();
-  double base = 0.0;
-  for (int w = 0; w < wave; ++w) base += sh_wave[w];
-  sh_incl[threadIdx.x] = base + x;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    double base = 0.0;
+    for (int w = 0; w < wave; ++w) base += sh_wave[k][w];
+    sh_incl[k][threadIdx.x] = base + x[k];
+  }
   __syncthreads();
 }
 
@@ -176,10 +194,25 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
   const int lo = c * kSub * U;
   const int hi = min(a.V, lo + kSub * U);
 
+  // The row's draft (clean row i < K verifies draft i; MASK row i proposed
+  // it; clean row K has none): the thread whose registers hold its logit
+  // records it, so the decision needs no second round of loads.
+  const int di = rho < a.N ? rho : rho - a.N;
+  const int xd = (!a.greedy && di < a.K) ? min(a.drafts[(size_t)b * a.K + di], a.V - 1) : -1;
+
   // All of this thread's loads first, then the arithmetic.
   float x[U][8];
 #pragma unroll
   for (int k = 0; k < U; ++k) load8<VEC, F32>(row, lo + k * kSub + 8 * tid, hi, x[k]);
+  if (xd >= lo && xd < hi && ((xd - lo) % kSub) / 8 == tid) {
+    const int kd = (xd - lo) / kSub, ed = xd % 8;
+    float val = 0.f;
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) val = (k == kd && e == ed) ? x[k][e] : val;
+    a.dlog[(size_t)b * a.R + rho] = val;
+  }
 
   double2 res;
   if (a.greedy) {
@@ -258,21 +291,23 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* out_plan, int* out_k
   // One round of independent loads: the slice statistics and the drafts.
   if (st_in_lds)
     for (int i = tid; i < nst; i += 256) sh_st[i] = st_g[i];
-  if (tid < K) sh_ids[tid] = a.drafts[(size_t)b * K + tid];
+  double lp = 0.0, lq = 0.0;  // the draft's raw logits, recorded by accept_stats
+  if (tid < K) {
+    sh_ids[tid] = a.drafts[(size_t)b * K + tid];
+    if (!a.greedy) {
+      lp = (double)a.dlog[(size_t)b * R + tid];
+      lq = (double)a.dlog[(size_t)b * R + N + tid];
+    }
+  }
   __syncthreads();
-  // The draft logits (second round) while the rows merge.
-  double lp = 0.0, lq = 0.0;
   bool listed = false;
   if (tid < K) {
     listed = true;  // no -1 terminator up to this draft
     for (int i = 0; i <= tid; ++i) listed = listed && (sh_ids[i] >= 0);
-    if (listed && !a.greedy) {
-      const int x = min(sh_ids[tid], a.V - 1);  // out-of-range ids are flagged
-      lp = (double)load1(row_ptr(a, b, tid), x, a.f32);
-      lq = (double)load1(row_ptr(a, b, N + tid), x, a.f32);
-    }
   }
-  // Row merge: thread rho walks its S1 slices in order.
+  // Row merge.  Row maxima first (thread rho, slices in order); then, when
+  // the statistics sit in LDS, every (row, slice) weight exp2((m_k - M) c)
+  // is formed by its own thread, and thread rho sums them in slice order.
   if (tid < R) {
     const double2* st = st_in_lds ? sh_st + tid * a.S1 : st_g + tid * a.S1;
     if (a.greedy) {
@@ -287,12 +322,28 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* out_plan, int* out_k
     } else {
       double M = -INFINITY;
       for (int k = 0; k < a.S1; ++k) M = fmax(M, st[k].x);
-      double S = 0.0;
-      for (int k = 0; k < a.S1; ++k) {
-        const double2 v = st[k];
-        if (v.x != -INFINITY) S += v.y * exp2((v.x - M) * (double)a.c2);
-      }
       sh_m[tid] = M;
+      if (!st_in_lds) {
+        double S = 0.0;
+        for (int k = 0; k < a.S1; ++k) {
+          const double2 v = st[k];
+          if (v.x != -INFINITY) S += v.y * exp2((v.x - M) * (double)a.c2);
+        }
+        sh_s[tid] = S;
+      }
+    }
+  }
+  if (st_in_lds && !a.greedy) {
+    __syncthreads();
+    for (int i = tid; i < nst; i += 256) {
+      const double2 v = sh_st[i];
+      const double M = sh_m[i / a.S1];
+      sh_st[i].y = (v.x != -INFINITY) ? v.y * exp2((v.x - M) * (double)a.c2) : 0.0;
+    }
+    __syncthreads();
+    if (tid < R) {
+      double S = 0.0;
+      for (int k = 0; k < a.S1; ++k) S += sh_st[tid * a.S1 + k].y;
       sh_s[tid] = S;
     }
   }
@@ -382,40 +433,40 @@ __device__ void write_prefix(const AccArgs& a, int b, const SamplePlan& sp, int 
 // Kernel 2: decision + sub-chunk sums of the sampling weights.
 // ---------------------------------------------------------------------------
 
-// Sampling weights of 8 elements (mode 0 residual, 1 p only).  Exponentials
-// are float32; the normalisation and the difference p - q are float64, so p
-// and q keep exactly the scales their row sums gave them and the residual
-// carries no systematic float32 scale error.
+// Sampling weights of 8 elements, scaled by the p row's sum S_p (sampling is
+// scale-free: t and the running sums scale together).  Mode 1 (p only):
+// w = exp2((l_p - m_p) c).  Mode 0 (residual): w = max(0, e_p - e_q * S_p/S_q)
+// with the ratio applied as a two-float product (hi + lo), so p and q keep
+// the exact relative scale their float64 row sums gave them and the
+// residual carries no systematic float32 scale error; what remains is the
+// per-element rounding of the float32 exponentials.
 __device__ inline void weights8(const AccArgs& a, const SamplePlan& sp, int mode,
                                 const float xp[8], const float xq[8], double w[8]) {
   const float c2 = a.c2;
   const float mp = (float)sp.mp;
-  const double ip = 1.0 / sp.sp;
   if (mode == 0) {
     const float mq = (float)sp.mq;
-    const double iq = 1.0 / sp.sq;
+    const double r = sp.sp / sp.sq;
+    const float r_hi = (float)r;
+    const float r_lo = (float)(r - (double)r_hi);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      w[e] = fmax(0.0, (double)__builtin_amdgcn_exp2f((xp[e] - mp) * c2) * ip -
-                           (double)__builtin_amdgcn_exp2f((xq[e] - mq) * c2) * iq);
+    for (int e = 0; e < 8; ++e) {
+      const float ep = __builtin_amdgcn_exp2f((xp[e] - mp) * c2);
+      const float eq = __builtin_amdgcn_exp2f((xq[e] - mq) * c2);
+      w[e] = (double)fmaxf(0.f, ep - fmaf(eq, r_hi, eq * r_lo));
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = (double)__builtin_amdgcn_exp2f((xp[e] - mp) * c2) * ip;
+    for (int e = 0; e < 8; ++e) w[e] = (double)__builtin_amdgcn_exp2f((xp[e] - mp) * c2);
   }
 }
 
-// Thread sums of one sub-chunk and their work-group inclusive scan (total
-// returned).  The same code recomputes a sub-chunk bit for bit in
-// accept_select.
-__device__ inline double subchunk_scan(const AccArgs& a, const SamplePlan& sp, int mode,
-                                       const float xp[8], const float xq[8], double w[8],
-                                       double* sh_wave, double* sh_incl) {
-  weights8(a, sp, mode, xp, xq, w);
+// This thread's sum of its 8 weights, accumulated in a fixed order.
+__device__ inline double thread_sum(const double w[8]) {
   double ts = 0.0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ts += w[e];
-  wg_scan_incl(ts, sh_wave, sh_incl);
-  return sh_incl[255];
+  return ts;
 }
 
 // This thread's 8 logits of sub-chunk sc in the p row (and q row, mode 0).
@@ -434,43 +485,44 @@ __device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, i
 
 constexpr int kMaxSpw = 4;  // upper bound of AcceptPlan::spw
 
-// One work-group per sequence: the decision, the kept prefix and the plan.
-__global__ __launch_bounds__(256) void accept_decide_kernel(AccArgs a) {
+// The decision (recomputed by every work-group of the sequence from the
+// slice statistics and recorded draft logits: one round of loads), then the
+// sub-chunk sums of the sampling weights.  The sequence's first work-group
+// also writes the kept prefix, the accept length and the plan.
+template <bool VEC, bool F32>
+__global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
   __shared__ double2 sh_st[kDecideStats];
   __shared__ double sh_draft[16][4];
   __shared__ double sh_m[32], sh_s[32];
   __shared__ int sh_ids[16];
   __shared__ SamplePlan sh_plan;
   __shared__ int sh_kp;
-  const int b = blockIdx.x;
-  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_m, sh_s, sh_ids, sh_st);
-  write_prefix(a, b, sh_plan, sh_kp, sh_draft, sh_ids);
-  if (threadIdx.x == 0) a.plan[b] = sh_plan;
-}
-
-// Sub-chunk sums of the sampling weights: every load of the work-group's
-// sub-chunks is issued right after the plan arrives.
-template <bool VEC, bool F32>
-__global__ __launch_bounds__(256) void accept_sum_kernel(AccArgs a) {
-  __shared__ double sh_wave[4], sh_incl[256];
+  __shared__ double sh_wave[kMaxSpw][4], sh_incl[kMaxSpw][256];
   const int tid = threadIdx.x;
   const int b = (int)(blockIdx.x / a.S2);
   const int w0 = (int)(blockIdx.x % a.S2);
-  const SamplePlan sp = a.plan[b];
-  if (sp.mode == 2) return;  // greedy: nothing to sample
+  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_m, sh_s, sh_ids, sh_st);
+  const SamplePlan sp = sh_plan;
+  if (w0 == 0) {
+    write_prefix(a, b, sp, sh_kp, sh_draft, sh_ids);
+    if (tid == 0) a.plan[b] = sp;
+  }
+  if (sp.mode == 2) return;  // greedy: the decision already wrote the token
+
   const int sc_lo = w0 * a.spw, n = min(a.nsub - sc_lo, a.spw);
   float xp[kMaxSpw][8], xq[kMaxSpw][8];
 #pragma unroll
   for (int k = 0; k < kMaxSpw; ++k)  // clamped, unconditional: all loads in flight together
     load_sub<VEC, F32>(a, b, sp, sp.mode, sc_lo + min(k, n - 1), xp[k], xq[k]);
-  double w[8];
-  double* subs = a.subsum + (size_t)b * a.nsub;
+  double ts[kMaxSpw];
 #pragma unroll
-  for (int k = 0; k < kMaxSpw; ++k)
-    if (k < n) {
-      const double tot = subchunk_scan(a, sp, sp.mode, xp[k], xq[k], w, sh_wave, sh_incl);
-      if (tid == 0) subs[sc_lo + k] = tot;
-    }
+  for (int k = 0; k < kMaxSpw; ++k) {
+    double w[8];
+    weights8(a, sp, sp.mode, xp[k], xq[k], w);
+    ts[k] = thread_sum(w);
+  }
+  wg_scan_incl<kMaxSpw>(ts, sh_wave, sh_incl);
+  if (tid < n) a.subsum[(size_t)b * a.nsub + sc_lo + tid] = sh_incl[tid][255];
 }
 
 // ---------------------------------------------------------------------------
@@ -478,7 +530,7 @@ __global__ __launch_bounds__(256) void accept_sum_kernel(AccArgs a) {
 // ---------------------------------------------------------------------------
 template <bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
-  __shared__ double sh_wave[4], sh_incl[256];
+  __shared__ double sh_wave[1][4], sh_incl[1][256];
   __shared__ double sh_sub[kMaxSubChunks];
   __shared__ double sh_t, sh_base, sh_W;
   __shared__ int sh_sc, sh_past, sh_mode;
@@ -503,8 +555,10 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
     // The residual vanished to rounding: fall back to p_j over the whole row.
     for (int sc = 0; sc < a.nsub; ++sc) {
       load_sub<VEC, F32>(a, b, sp, 1, sc, xp, xq);
-      const double tot = subchunk_scan(a, sp, 1, xp, xq, w, sh_wave, sh_incl);
-      if (tid == 0) sh_sub[sc] = tot;
+      weights8(a, sp, 1, xp, xq, w);
+      const double ts[1] = {thread_sum(w)};
+      wg_scan_incl<1>(ts, sh_wave, sh_incl);
+      if (tid == 0) sh_sub[sc] = sh_incl[0][255];
     }
     __syncthreads();
     if (tid == 0) {
@@ -540,7 +594,11 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   const double t = sh_t, base = sh_base;
   const int sc = sh_sc, mode = sh_mode;
   load_sub<VEC, F32>(a, b, sp, mode, sc, xp, xq);
-  subchunk_scan(a, sp, mode, xp, xq, w, sh_wave, sh_incl);
+  weights8(a, sp, mode, xp, xq, w);
+  {
+    const double ts[1] = {thread_sum(w)};
+    wg_scan_incl<1>(ts, sh_wave, sh_incl);  // the same per-sub-chunk scan as accept_decide_sum
+  }
   const int v0 = sc * kSub + 8 * tid;
   int lastp = -1;
 #pragma unroll
@@ -549,8 +607,8 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   if (!sh_past) {
     // Thread k owns [base + incl[k-1], base + incl[k]): the intervals tile
     // [base, base + total) exactly, so exactly one thread holds t.
-    const double lo = base + (tid ? sh_incl[tid - 1] : 0.0);
-    const double hi = base + sh_incl[tid];
+    const double lo = base + (tid ? sh_incl[0][tid - 1] : 0.0);
+    const double hi = base + sh_incl[0][tid];
     if (lo <= t && t < hi) {
       double run = lo;
       int tok = lastp;
@@ -598,12 +656,12 @@ int32_t launch_all(AccArgs a, int U1, hipStream_t s) {
     default: r = launch_stats<1, VEC, F32>(a, s); break;
   }
   if (r != IDLM_OK) return r;
-  hipLaunchKernelGGL(accept_decide_kernel, dim3((unsigned)a.B), dim3(256), 0, s, a);
-  if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
-  if (a.greedy) return IDLM_OK;  // the decision already wrote the argmax tokens
+  // Greedy needs one decision work-group per sequence and no sampling.
+  if (a.greedy) a.S2 = 1;
   const int64_t g2 = (int64_t)a.B * a.S2;
-  hipLaunchKernelGGL((accept_sum_kernel<VEC, F32>), dim3((unsigned)g2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((accept_decide_sum_kernel<VEC, F32>), dim3((unsigned)g2), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
+  if (a.greedy) return IDLM_OK;
   hipLaunchKernelGGL((accept_select_kernel<VEC, F32>), dim3((unsigned)a.B), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
@@ -630,6 +688,7 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.stats = (double2*)(ws + p.off_stats);
   a.plan = (SamplePlan*)(ws + p.off_splan);
   a.subsum = (double*)(ws + p.off_subsum);
+  a.dlog = (float*)(ws + p.off_dlog);
   a.B = d.B;
   a.N = d.N;
   a.K = d.N - 1;

@@ -83,6 +83,8 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   o = align256(o + (size_t)d.B * c.R * c.S1 * 16);
   p->off_subsum = o;
   o = align256(o + (size_t)d.B * c.nsub * 8);
+  p->off_dlog = o;
+  o = align256(o + (size_t)d.B * c.R * 4);
   p->total = o;
   return true;
 }
