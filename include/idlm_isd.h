@@ -35,8 +35,11 @@
  *   on the host: kernels clamp the value, set a sticky status word in the
  *   workspace and leave that sequence's outputs unspecified.  Read it with
  *   idlm_isd_read_status.
- * - Calls on one workspace must not overlap (they share its counters); use
- *   one workspace per concurrent stream.
+ * - Calls on one workspace must not overlap (they share its partial
+ *   softmax states, row statistics and sampling plans); use one workspace
+ *   per concurrent stream.  The kernels use no atomic counters: launch
+ *   boundaries order every hand-over, so results do not depend on
+ *   scheduling.
  *
  * Symbols: B batch, N stride, R = 2N-1 query rows, K = N-1 drafts, Hq / Hkv
  * query / KV heads, G = Hq/Hkv, D head dim, V vocabulary, P pool pages.
@@ -101,10 +104,10 @@ size_t idlm_isd_workspace_bytes(const idlm_isd_dims* d);
  * IDLM_ERR_TEMPERATURE.  Host only. */
 int32_t idlm_isd_validate(const idlm_isd_dims* d, float T);
 
-/* Prepare a workspace for first use: clears its counters and status word
- * with a fill kernel on `stream`.  Must run once after allocating (or after
- * any foreign write to) the workspace; the step kernels return every counter
- * to zero themselves. */
+/* Prepare a workspace for first use: zeroes it (the sticky status word
+ * included) with a fill kernel on `stream`, never a memset node.  Must run
+ * once after allocating the workspace, and again to clear a reported device
+ * data error; the step kernels need nothing else zeroed between calls. */
 int32_t idlm_isd_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 
 /* Causal paged GQA attention of the R step rows (see the header comment).

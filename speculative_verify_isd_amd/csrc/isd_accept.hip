@@ -9,30 +9,34 @@
 // guarantee holds) and the committed prefix ends there; with every draft
 // kept, the last clean row supplies a bonus token.
 //
-// Three launches; kernel boundaries are the only synchronisation (no
-// atomics, no fences), and every reduction runs in a fixed order, so results
-// do not depend on scheduling:
+// Three launches; kernel boundaries are the only synchronisation between
+// work-groups (no atomic counters, no fences), and every reduction runs in a
+// fixed order, so results do not depend on scheduling:
 //
 //   accept_stats       grid B*R*S1.  Each work-group reduces one slice of one
 //                      logit row to (max m, sum of exp2((l - m) c)) with
 //                      c = log2(e)/T: every load of the slice is issued before
-//                      any arithmetic, the slice max is reduced first so each
-//                      element costs one float32 exponential, sums are
-//                      float64.  The slice holding the row's draft also
-//                      records the draft's logit.  Greedy (T = 0): (max,
-//                      lowest argmax).
-//   accept_decide_sum  grid B*S2.  Every work-group of a sequence merges the
-//                      slices of each row in order, evaluates p_i(x_i) and
-//                      q_i(x_i) in float64, draws the Philox uniforms and runs
-//                      the sequential ratio test (one round of loads), then
-//                      sums the sampling weights (residual max(0, p_j - q_j)
-//                      or bonus p) of its 2048-element sub-chunks.  The first
-//                      work-group writes the kept prefix, the accept length
-//                      and the sampling plan (the whole answer when T = 0).
-//   accept_select      grid B.  Prefixes the sub-chunk sums in order, finds
-//                      the sub-chunk holding t = u' * sum(w), recomputes it
-//                      bit for bit and scans it to the smallest v whose
-//                      running sum exceeds t.
+//                      any arithmetic and the logits stay packed in registers,
+//                      the slice max is reduced first so each element costs
+//                      one float32 exponential, sums are float64.  The slice
+//                      holding the row's draft also records the draft's
+//                      logit.  Greedy (T = 0): (max, lowest argmax).
+//   accept_decide_sum  grid B*S2, S2 sized so the grid fits on the chip at
+//                      once.  In every work-group of a sequence, wave 0 alone
+//                      merges the slices of each row (a lane group per row,
+//                      butterfly reductions), evaluates p_i(x_i) and q_i(x_i)
+//                      in float64, draws the Philox uniforms while those
+//                      loads are in flight and finds the first rejection with
+//                      two ballots; one barrier hands the plan to the other
+//                      waves.  The work-group then sums the sampling weights
+//                      (residual max(0, p_j - q_j) or bonus p) of its
+//                      2048-element sub-chunks.  The first work-group writes
+//                      the kept prefix, the accept length and the plan (the
+//                      whole answer when T = 0).
+//   accept_select      grid B.  Wave 0 prefixes the sub-chunk sums, finds the
+//                      sub-chunk holding t = u' * sum(w); the work-group
+//                      recomputes that sub-chunk's weights bit for bit and
+//                      scans it to the smallest v whose running sum exceeds t.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -91,7 +95,7 @@ struct AccArgs {
   SamplePlan* plan; // [B]
   double* subsum;   // [B][nsub]
   float* dlog;      // [B][R]: raw logit of the row's draft (rows that verify or proposed one)
-  int B, N, K, R, V, S1, nsub, spw, S2, f32;
+  int B, N, K, R, V, S1, nsub, spw, S2, f32;  // spw, S2: chosen at launch
 };
 
 // Row rho of sequence b: rho < N is clean row rho, otherwise MASK row rho - N.
@@ -105,36 +109,51 @@ __device__ inline float load1(const void* row, int v, int f32) {
   return f32 ? ((const float*)row)[v] : __uint_as_float(((unsigned)((const u16*)row)[v]) << 16);
 }
 
-// Eight consecutive logits starting at v; elements at or past hi read as
-// -inf.  VEC (rows 16-byte aligned, V a multiple of 8, so v and hi are
-// multiples of 8): one vector load, from a clamped in-row address when the
-// group lies past hi, with no branch, so a thread's loads can all be in
-// flight together.  Otherwise element by element.
+// Eight consecutive logits as loaded.  bf16 rows on the vector path stay
+// packed two to a register until used, which halves the registers a batch of
+// loads occupies; float32 rows and the element-wise path hold float bits.
 template <bool VEC, bool F32>
-__device__ inline void load8(const void* row, int v, int hi, float x[8]) {
-  if (VEC) {
+struct Logits8 {
+  static constexpr bool kPacked = VEC && !F32;
+  static constexpr int NW = kPacked ? 4 : 8;
+  unsigned w[NW];
+  __device__ float operator[](int e) const {
+    if constexpr (kPacked)
+      return __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+    else
+      return __uint_as_float(w[e]);
+  }
+};
+
+// Logits v .. v+7 of a row; elements at or past hi read as -inf.  VEC (rows
+// 16-byte aligned, V a multiple of 8, so v and hi are multiples of 8): one
+// vector load, from a clamped in-row address when the group lies past hi,
+// with no branch, so a thread's loads can all be in flight together.
+// Otherwise element by element.
+template <bool VEC, bool F32>
+__device__ inline Logits8<VEC, F32> load8(const void* row, int v, int hi) {
+  Logits8<VEC, F32> r;
+  if constexpr (VEC) {
     const bool in = v < hi;
     const int vi = in ? v : hi - 8;
-    if (F32) {
-      const float4 p0 = *(const float4*)((const float*)row + vi);
-      const float4 p1 = *(const float4*)((const float*)row + vi + 4);
-      x[0] = p0.x; x[1] = p0.y; x[2] = p0.z; x[3] = p0.w;
-      x[4] = p1.x; x[5] = p1.y; x[6] = p1.z; x[7] = p1.w;
+    if constexpr (F32) {
+      const uint4 p0 = *(const uint4*)((const float*)row + vi);
+      const uint4 p1 = *(const uint4*)((const float*)row + vi + 4);
+      const unsigned w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r.w[e] = in ? w[e] : 0xFF800000u;
     } else {
       const uint4 p = *(const uint4*)((const u16*)row + vi);
       const unsigned w[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(w[e] << 16);
-        x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-      }
+      for (int e = 0; e < 4; ++e) r.w[e] = in ? w[e] : 0xFF80FF80u;  // two bf16 -inf
     }
+  } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = in ? x[e] : -INFINITY;
-    return;
+    for (int e = 0; e < 8; ++e)
+      r.w[e] = (v + e < hi) ? __float_as_uint(load1(row, v + e, F32)) : 0xFF800000u;
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = (v + e < hi) ? load1(row, v + e, F32) : -INFINITY;
+  return r;
 }
 
 // Greedy order: larger value wins, lower index on ties.
@@ -145,35 +164,34 @@ __device__ inline void better(float& bv, int& bi, float v, int i) {
   }
 }
 
-// Inclusive scans of NS doubles per thread over the work-group, run side by
-// side (one scan per index k, each in the same fixed order whatever NS is):
-// thread t's inclusive value for scan k lands in sh_incl[k][t].
-template <int NS>
-__device__ inline void wg_scan_incl(const double (&x0)[NS], double (*sh_wave)[4],
-                                    double (*sh_incl)[256]) {
+// Inclusive scan of one double per thread over the work-group: thread t's
+// inclusive value lands in sh_incl[t].  Within a wave the scan takes lane
+// offsets 1, 2, ..., 32 in turn, so the value at lane 63 is the same sum, in
+// the same association, as the xor butterfly of wave_total(); across waves
+// the partial totals are added in wave order.
+__device__ inline void wg_scan_incl(double x, double* sh_wave, double* sh_incl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double x[NS];
-#pragma unroll
-  for (int k = 0; k < NS; ++k) x[k] = x0[k];
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      const double y = __shfl_up(x[k], off);
-      if (lane >= off) x[k] += y;
-    }
+    const double y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  if (lane == 63)
-#pragma unroll
-    for (int k = 0; k < NS; ++k) sh_wave[k][wave] = x[k];
+  if (lane == 63) sh_wave[wave] = x;
   __syncthreads();
-#pragma unroll
-  for (int k = 0; k < NS; ++k) {
-    double base = 0.0;
-    for (int w = 0; w < wave; ++w) base += sh_wave[k][w];
-    sh_incl[k][threadIdx.x] = base + x[k];
-  }
+  double base = 0.0;
+  for (int w = 0; w < wave; ++w) base += sh_wave[w];
+  sh_incl[threadIdx.x] = base + x;
   __syncthreads();
+}
+
+// The wave's total of x, read at lane 63: the xor butterfly over offsets 1,
+// 2, ..., 32 adds, at lane 63, exactly the operands the inclusive scan above
+// adds there (lane 63 - off holds the same partial sum in both), so the
+// totals agree bit for bit.
+__device__ inline double wave_total(double x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -201,9 +219,9 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
   const int xd = (!a.greedy && di < a.K) ? min(a.drafts[(size_t)b * a.K + di], a.V - 1) : -1;
 
   // All of this thread's loads first, then the arithmetic.
-  float x[U][8];
+  Logits8<VEC, F32> x[U];
 #pragma unroll
-  for (int k = 0; k < U; ++k) load8<VEC, F32>(row, lo + k * kSub + 8 * tid, hi, x[k]);
+  for (int k = 0; k < U; ++k) x[k] = load8<VEC, F32>(row, lo + k * kSub + 8 * tid, hi);
   if (xd >= lo && xd < hi && ((xd - lo) % kSub) / 8 == tid) {
     const int kd = (xd - lo) / kSub, ed = xd % 8;
     float val = 0.f;
@@ -276,125 +294,131 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
 
 // ---------------------------------------------------------------------------
 // The sequence's decision, recomputed by every work-group that needs it.
-// Collective: all 256 threads call it.  Leaves the plan in *out_plan, the
-// draft count in *out_kp, the per-draft (p, q, u, u') in sh_draft and the
-// raw draft ids in sh_ids.
+// Collective: all threads call it; wave 0 does the work.  Leaves the plan in
+// *sh_plan, the draft count in *sh_kp, the per-draft (p, q, u, u') in
+// sh_draft and the raw draft ids in sh_ids.
 // ---------------------------------------------------------------------------
-__device__ void decide(const AccArgs& a, int b, SamplePlan* out_plan, int* out_kp,
-                       double (*sh_draft)[4], double* sh_m, double* sh_s, int* sh_ids,
-                       double2* sh_st) {
-  const int tid = threadIdx.x;
-  const int R = a.R, N = a.N, K = a.K;
-  const int nst = R * a.S1;
-  const bool st_in_lds = nst <= kDecideStats;
-  const double2* st_g = a.stats + (size_t)b * nst;
-  // One round of independent loads: the slice statistics and the drafts.
-  if (st_in_lds)
-    for (int i = tid; i < nst; i += 256) sh_st[i] = st_g[i];
-  double lp = 0.0, lq = 0.0;  // the draft's raw logits, recorded by accept_stats
-  if (tid < K) {
-    sh_ids[tid] = a.drafts[(size_t)b * K + tid];
-    if (!a.greedy) {
-      lp = (double)a.dlog[(size_t)b * R + tid];
-      lq = (double)a.dlog[(size_t)b * R + N + tid];
+constexpr int kStatCache = 4;  // slice statistics a lane keeps in registers
+
+__device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
+                       double (*sh_draft)[4], int* sh_ids) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int R = a.R, N = a.N, K = a.K, S1 = a.S1;
+    // L lanes per row (R rounded up to a power of two rows in one wave).
+    int rp = 1;
+    while (rp < R) rp <<= 1;
+    const int L = 64 / rp;
+    const int rho = lane / L, q = lane % L;
+    const bool row_ok = rho < R;
+    const double2* st = a.stats + ((size_t)b * R + (row_ok ? rho : 0)) * S1;
+
+    // One round of independent loads: this lane's slice statistics, and for
+    // lane i < K draft i and the logits recorded for it.
+    double2 cs[kStatCache];
+#pragma unroll
+    for (int j = 0; j < kStatCache; ++j) cs[j] = st[min(q + j * L, S1 - 1)];
+    int id = -1;
+    float lpf = 0.f, lqf = 0.f;
+    if (K > 0) {
+      const int ic = min(lane, K - 1);
+      id = a.drafts[(size_t)b * K + ic];
+      lpf = a.dlog[(size_t)b * R + ic];
+      lqf = a.dlog[(size_t)b * R + N + ic];
     }
-  }
-  __syncthreads();
-  bool listed = false;
-  if (tid < K) {
-    listed = true;  // no -1 terminator up to this draft
-    for (int i = 0; i <= tid; ++i) listed = listed && (sh_ids[i] >= 0);
-  }
-  // Row merge.  Row maxima first (thread rho, slices in order); then, when
-  // the statistics sit in LDS, every (row, slice) weight exp2((m_k - M) c)
-  // is formed by its own thread, and thread rho sums them in slice order.
-  if (tid < R) {
-    const double2* st = st_in_lds ? sh_st + tid * a.S1 : st_g + tid * a.S1;
+    // Philox while the loads are in flight: lane i draws (u_i, u'_i).
+    const U64x4 ph = philox4x64_10((uint64_t)lane, 0, 0, 0, a.seed, (uint64_t)b);
+    const double u = top24(ph.w[0]), u2 = top24(ph.w[1]);
+
+    // Row merge inside each L-lane group.  M (max) is exact in any order; S
+    // is summed by a fixed butterfly and read from the group's lane 0.
+    double M, S;
     if (a.greedy) {
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
-      for (int k = 0; k < a.S1; ++k) {
+#pragma unroll
+      for (int j = 0; j < kStatCache; ++j)
+        if (row_ok && q + j * L < S1) better(bv, bi, (float)cs[j].x, (int)cs[j].y);
+      for (int k = q + kStatCache * L; row_ok && k < S1; k += L) {
         const double2 v = st[k];
         better(bv, bi, (float)v.x, (int)v.y);
       }
-      sh_m[tid] = bv;
-      sh_s[tid] = (double)bi;
-    } else {
-      double M = -INFINITY;
-      for (int k = 0; k < a.S1; ++k) M = fmax(M, st[k].x);
-      sh_m[tid] = M;
-      if (!st_in_lds) {
-        double S = 0.0;
-        for (int k = 0; k < a.S1; ++k) {
-          const double2 v = st[k];
-          if (v.x != -INFINITY) S += v.y * exp2((v.x - M) * (double)a.c2);
-        }
-        sh_s[tid] = S;
+      for (int off = 1; off < L; off <<= 1) {
+        const float vo = __shfl_xor(bv, off);
+        const int io = __shfl_xor(bi, off);
+        better(bv, bi, vo, io);
       }
+      M = bv;
+      S = (double)bi;
+    } else {
+      M = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kStatCache; ++j)
+        if (row_ok && q + j * L < S1) M = fmax(M, cs[j].x);
+      for (int k = q + kStatCache * L; row_ok && k < S1; k += L) M = fmax(M, st[k].x);
+      for (int off = 1; off < L; off <<= 1) M = fmax(M, __shfl_xor(M, off));
+      const double c2 = (double)a.c2;
+      S = 0.0;
+#pragma unroll
+      for (int j = 0; j < kStatCache; ++j)
+        if (row_ok && q + j * L < S1 && cs[j].x != -INFINITY)
+          S += cs[j].y * exp2((cs[j].x - M) * c2);
+      for (int k = q + kStatCache * L; row_ok && k < S1; k += L) {
+        const double2 v = st[k];
+        if (v.x != -INFINITY) S += v.y * exp2((v.x - M) * c2);
+      }
+      for (int off = 1; off < L; off <<= 1) S += __shfl_xor(S, off);
     }
-  }
-  if (st_in_lds && !a.greedy) {
-    __syncthreads();
-    for (int i = tid; i < nst; i += 256) {
-      const double2 v = sh_st[i];
-      const double M = sh_m[i / a.S1];
-      sh_st[i].y = (v.x != -INFINITY) ? v.y * exp2((v.x - M) * (double)a.c2) : 0.0;
-    }
-    __syncthreads();
-    if (tid < R) {
-      double S = 0.0;
-      for (int k = 0; k < a.S1; ++k) S += sh_st[tid * a.S1 + k].y;
-      sh_s[tid] = S;
-    }
-  }
-  __syncthreads();
-  // Per-draft inputs of the ratio test, one thread per draft.
-  if (tid < K && listed) {
-    const int x = min(sh_ids[tid], a.V - 1);
-    const U64x4 w = philox4x64_10((uint64_t)tid, 0, 0, 0, a.seed, (uint64_t)b);
-    double p, q;
+
+    // Lane i < K: p_i(x_i) from clean row i, q_i(x_i) from MASK row i.
+    const int ia = min(lane, R - 1), ib = min(N + lane, R - 1);
+    const double Mp = __shfl(M, ia * L), Sp = __shfl(S, ia * L);
+    const double Mq = __shfl(M, ib * L), Sq = __shfl(S, ib * L);
+    const int x = min(id, a.V - 1);
+    double p, qq;
     if (a.greedy) {
-      p = (x == (int)sh_s[tid]) ? 1.0 : 0.0;
-      q = (x == (int)sh_s[N + tid]) ? 1.0 : 0.0;
+      p = (x == (int)Sp) ? 1.0 : 0.0;
+      qq = (x == (int)Sq) ? 1.0 : 0.0;
     } else {
-      p = exp((lp - sh_m[tid]) * a.invT) / sh_s[tid];
-      q = exp((lq - sh_m[N + tid]) * a.invT) / sh_s[N + tid];
+      p = exp(((double)lpf - Mp) * a.invT) / Sp;
+      qq = exp(((double)lqf - Mq) * a.invT) / Sq;
     }
-    sh_draft[tid][0] = p;
-    sh_draft[tid][1] = q;
-    sh_draft[tid][2] = top24(w.w[0]);
-    sh_draft[tid][3] = top24(w.w[1]);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int kp = K;
-    for (int i = 0; i < K; ++i)
-      if (sh_ids[i] < 0) {
-        kp = i;
-        break;
-      }
-    int j = kp;
-    for (int i = 0; i < kp; ++i) {
-      const double p = sh_draft[i][0], q = sh_draft[i][1], u = sh_draft[i][2];
-      if (!(p >= q || u * q < p)) {
-        j = i;
-        break;
-      }
+    // A negative id ends the list; the first rejection among the listed
+    // drafts ends the kept prefix.
+    const bool is_draft = lane < K;
+    const unsigned long long term = __ballot(is_draft && id < 0);
+    const int kp = term ? (int)__builtin_ctzll(term) : K;
+    const bool rej = is_draft && lane < kp && !(p >= qq || u * qq < p);
+    const unsigned long long rm = __ballot(rej);
+    const int j = rm ? (int)__builtin_ctzll(rm) : kp;
+
+    const bool resid = j < kp;
+    const double mp = __shfl(M, j * L), sp_ = __shfl(S, j * L);
+    const int jq = resid ? N + j : 0;
+    const double mq = __shfl(M, jq * L), sq = __shfl(S, jq * L);
+    const double u2j = __shfl(u2, j);
+    if (lane < K) {
+      sh_ids[lane] = id;
+      sh_draft[lane][0] = p;
+      sh_draft[lane][1] = qq;
+      sh_draft[lane][2] = u;
+      sh_draft[lane][3] = u2;
     }
-    SamplePlan sp;
-    sp.j = j;
-    sp.u2 = j < kp ? sh_draft[j][3]
-                   : top24(philox4x64_10((uint64_t)j, 0, 0, 0, a.seed, (uint64_t)b).w[1]);
-    sp.row_p = j;
-    sp.row_q = (j < kp) ? j : 0;
-    sp.mode = a.greedy ? 2 : ((j < kp) ? 0 : 1);
-    sp.mp = sh_m[j];
-    sp.sp = sh_s[j];
-    sp.mq = (j < kp) ? sh_m[N + j] : 0.0;
-    sp.sq = (j < kp) ? sh_s[N + j] : 1.0;
-    sp.pad = a.greedy ? sh_s[j] : 0.0;  // greedy: the clean argmax of row j
-    *out_plan = sp;
-    *out_kp = kp;
+    if (lane == 0) {
+      SamplePlan pl;
+      pl.mode = a.greedy ? 2 : (resid ? 0 : 1);
+      pl.row_p = j;
+      pl.row_q = resid ? j : 0;
+      pl.j = j;
+      pl.mp = mp;
+      pl.sp = sp_;
+      pl.mq = resid ? mq : 0.0;
+      pl.sq = resid ? sq : 1.0;
+      pl.u2 = u2j;
+      pl.pad = a.greedy ? sp_ : 0.0;  // greedy: the clean argmax of row j
+      *sh_plan = pl;
+      *sh_kp = kp;
+    }
   }
   __syncthreads();
 }
@@ -440,8 +464,10 @@ __device__ void write_prefix(const AccArgs& a, int b, const SamplePlan& sp, int 
 // the exact relative scale their float64 row sums gave them and the
 // residual carries no systematic float32 scale error; what remains is the
 // per-element rounding of the float32 exponentials.
+template <bool VEC, bool F32>
 __device__ inline void weights8(const AccArgs& a, const SamplePlan& sp, int mode,
-                                const float xp[8], const float xq[8], double w[8]) {
+                                const Logits8<VEC, F32>& xp, const Logits8<VEC, F32>& xq,
+                                double w[8]) {
   const float c2 = a.c2;
   const float mp = (float)sp.mp;
   if (mode == 0) {
@@ -472,18 +498,19 @@ __device__ inline double thread_sum(const double w[8]) {
 // This thread's 8 logits of sub-chunk sc in the p row (and q row, mode 0).
 template <bool VEC, bool F32>
 __device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, int mode, int sc,
-                                float xp[8], float xq[8]) {
+                                Logits8<VEC, F32>& xp, Logits8<VEC, F32>& xq) {
   const int v = sc * kSub + 8 * threadIdx.x;
-  load8<VEC, F32>(row_ptr(a, b, sp.row_p), v, a.V, xp);
+  xp = load8<VEC, F32>(row_ptr(a, b, sp.row_p), v, a.V);
   if (mode == 0) {
-    load8<VEC, F32>(row_ptr(a, b, a.N + sp.row_q), v, a.V, xq);
+    xq = load8<VEC, F32>(row_ptr(a, b, a.N + sp.row_q), v, a.V);
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xq[e] = -INFINITY;
+    for (int e = 0; e < Logits8<VEC, F32>::NW; ++e)
+      xq.w[e] = Logits8<VEC, F32>::kPacked ? 0xFF80FF80u : 0xFF800000u;
   }
 }
 
-constexpr int kMaxSpw = 4;  // upper bound of AcceptPlan::spw
+constexpr int kMaxSpw = 4;  // most sub-chunks one summing work-group takes
 
 // The decision (recomputed by every work-group of the sequence from the
 // slice statistics and recorded draft logits: one round of loads), then the
@@ -491,17 +518,15 @@ constexpr int kMaxSpw = 4;  // upper bound of AcceptPlan::spw
 // also writes the kept prefix, the accept length and the plan.
 template <bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
-  __shared__ double2 sh_st[kDecideStats];
   __shared__ double sh_draft[16][4];
-  __shared__ double sh_m[32], sh_s[32];
   __shared__ int sh_ids[16];
   __shared__ SamplePlan sh_plan;
   __shared__ int sh_kp;
-  __shared__ double sh_wave[kMaxSpw][4], sh_incl[kMaxSpw][256];
-  const int tid = threadIdx.x;
+  __shared__ double sh_wave[kMaxSpw][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = (int)(blockIdx.x / a.S2);
   const int w0 = (int)(blockIdx.x % a.S2);
-  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_m, sh_s, sh_ids, sh_st);
+  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_ids);
   const SamplePlan sp = sh_plan;
   if (w0 == 0) {
     write_prefix(a, b, sp, sh_kp, sh_draft, sh_ids);
@@ -510,30 +535,96 @@ __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
   if (sp.mode == 2) return;  // greedy: the decision already wrote the token
 
   const int sc_lo = w0 * a.spw, n = min(a.nsub - sc_lo, a.spw);
-  float xp[kMaxSpw][8], xq[kMaxSpw][8];
+  Logits8<VEC, F32> xp[kMaxSpw], xq[kMaxSpw];
 #pragma unroll
   for (int k = 0; k < kMaxSpw; ++k)  // clamped, unconditional: all loads in flight together
     load_sub<VEC, F32>(a, b, sp, sp.mode, sc_lo + min(k, n - 1), xp[k], xq[k]);
-  double ts[kMaxSpw];
 #pragma unroll
   for (int k = 0; k < kMaxSpw; ++k) {
     double w[8];
-    weights8(a, sp, sp.mode, xp[k], xq[k], w);
-    ts[k] = thread_sum(w);
+    weights8<VEC, F32>(a, sp, sp.mode, xp[k], xq[k], w);
+    const double tot = wave_total(thread_sum(w));
+    if (lane == 63) sh_wave[k][wave] = tot;
   }
-  wg_scan_incl<kMaxSpw>(ts, sh_wave, sh_incl);
-  if (tid < n) a.subsum[(size_t)b * a.nsub + sc_lo + tid] = sh_incl[tid][255];
+  __syncthreads();
+  // The same total, in the same association, as thread 255's inclusive scan
+  // value in accept_select.
+  if (tid < n)
+    a.subsum[(size_t)b * a.nsub + sc_lo + tid] =
+        ((sh_wave[tid][0] + sh_wave[tid][1]) + sh_wave[tid][2]) + sh_wave[tid][3];
 }
 
 // ---------------------------------------------------------------------------
 // Kernel 3: locate t and scan one sub-chunk.
 // ---------------------------------------------------------------------------
+
+// Wave 0 locates the sub-chunk holding t = u' * W, W = the sum of sh_sub.
+// Lane l takes a contiguous run of sub-chunks; the runs' sums are prefixed by
+// an inclusive wave scan; each lane then walks its run from its exclusive
+// prefix.  The chosen sub-chunk is the first with a positive sum whose end
+// exceeds t (base = its start); with no such sub-chunk (t at or past the
+// total by rounding) it is the last sub-chunk with a positive sum and *past
+// is set.  Results go to the shared variables; the caller synchronises.
+__device__ void locate(const double* sh_sub, int nsub, double u2, double* sh_W, double* sh_t,
+                       double* sh_base, int* sh_sc, int* sh_past) {
+  const int lane = threadIdx.x;
+  const int per = (nsub + 63) / 64;
+  const int k0 = min(nsub, lane * per), k1 = min(nsub, k0 + per);
+  double ls = 0.0;
+  int lastpos = -1;
+  for (int k = k0; k < k1; ++k) {
+    const double v = sh_sub[k];
+    ls += v;
+    if (v > 0.0) lastpos = k;
+  }
+  double inc = ls;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  const double W = __shfl(inc, 63);
+  double ex = __shfl_up(inc, 1);
+  if (lane == 0) ex = 0.0;
+  const double t = u2 * W;
+  double run = ex, hbase = 0.0;
+  int hit = -1;
+  for (int k = k0; k < k1; ++k) {
+    const double v = sh_sub[k];
+    const double nx = run + v;
+    if (hit < 0 && v > 0.0 && nx > t) {
+      hit = k;
+      hbase = run;
+    }
+    run = nx;
+  }
+  const unsigned long long hm = __ballot(hit >= 0);
+  int sel = 0, past = 0;
+  double base = 0.0;
+  if (hm) {
+    const int src = (int)__builtin_ctzll(hm);
+    sel = __shfl(hit, src);
+    base = __shfl(hbase, src);
+  } else {
+    past = 1;
+    const unsigned long long pm = __ballot(lastpos >= 0);
+    if (pm) sel = __shfl(lastpos, 63 - (int)__builtin_clzll(pm));
+  }
+  if (lane == 0) {
+    *sh_W = W;
+    *sh_t = t;
+    *sh_base = base;
+    *sh_sc = sel;
+    *sh_past = past;
+  }
+}
+
 template <bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
-  __shared__ double sh_wave[1][4], sh_incl[1][256];
+  __shared__ double sh_wave[4], sh_incl[256];
   __shared__ double sh_sub[kMaxSubChunks];
   __shared__ double sh_t, sh_base, sh_W;
-  __shared__ int sh_sc, sh_past, sh_mode;
+  __shared__ int sh_sc, sh_past;
   __shared__ int found_tok, found_last;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -541,74 +632,47 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   for (int i = tid; i < a.nsub; i += 256) sh_sub[i] = subs[i];
   const SamplePlan sp = a.plan[b];
   if (sp.mode == 2) return;
-  float xp[8], xq[8];
-  double w[8];
-  __syncthreads();
   if (tid == 0) {
-    double W = 0.0;
-    for (int sc = 0; sc < a.nsub; ++sc) W += sh_sub[sc];
-    sh_W = W;
-    sh_mode = sp.mode;
-  }
-  __syncthreads();
-  if (!(sh_W > 0.0)) {
-    // The residual vanished to rounding: fall back to p_j over the whole row.
-    for (int sc = 0; sc < a.nsub; ++sc) {
-      load_sub<VEC, F32>(a, b, sp, 1, sc, xp, xq);
-      weights8(a, sp, 1, xp, xq, w);
-      const double ts[1] = {thread_sum(w)};
-      wg_scan_incl<1>(ts, sh_wave, sh_incl);
-      if (tid == 0) sh_sub[sc] = sh_incl[0][255];
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double W = 0.0;
-      for (int sc = 0; sc < a.nsub; ++sc) W += sh_sub[sc];
-      sh_W = W;
-      sh_mode = 1;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const double t = sp.u2 * sh_W;
-    double cum = 0.0, base = 0.0;
-    int sel = -1, lastpos = 0;
-    for (int sc = 0; sc < a.nsub; ++sc) {
-      const double nx = cum + sh_sub[sc];
-      if (sh_sub[sc] > 0.0) lastpos = sc;
-      if (sel < 0 && nx > t) {
-        sel = sc;
-        base = cum;
-      }
-      cum = nx;
-    }
-    sh_past = sel < 0;  // rounding put t at or past the total
-    if (sel < 0) sel = lastpos;
-    sh_t = t;
-    sh_base = base;
-    sh_sc = sel;
     found_tok = 0x7FFFFFFF;
     found_last = -1;
   }
+  Logits8<VEC, F32> xp, xq;
+  double w[8];
+  int mode = sp.mode;
   __syncthreads();
-  const double t = sh_t, base = sh_base;
-  const int sc = sh_sc, mode = sh_mode;
-  load_sub<VEC, F32>(a, b, sp, mode, sc, xp, xq);
-  weights8(a, sp, mode, xp, xq, w);
-  {
-    const double ts[1] = {thread_sum(w)};
-    wg_scan_incl<1>(ts, sh_wave, sh_incl);  // the same per-sub-chunk scan as accept_decide_sum
+  if (tid < 64) locate(sh_sub, a.nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
+  __syncthreads();
+  if (!(sh_W > 0.0)) {
+    // The residual vanished to rounding: fall back to p_j over the whole row.
+    mode = 1;
+    for (int sc = 0; sc < a.nsub; ++sc) {
+      load_sub<VEC, F32>(a, b, sp, 1, sc, xp, xq);
+      weights8<VEC, F32>(a, sp, 1, xp, xq, w);
+      wg_scan_incl(thread_sum(w), sh_wave, sh_incl);
+      if (tid == 0) sh_sub[sc] = sh_incl[255];
+    }
+    __syncthreads();
+    if (tid < 64) locate(sh_sub, a.nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
+    __syncthreads();
   }
+  const double base = sh_base;
+  const int sc = sh_sc, past = sh_past;
+  // t sits in [base, base + sum of the sub-chunk) up to rounding at a
+  // sub-chunk boundary; clamping it to base keeps it inside.
+  const double t = fmax(sh_t, base);
+  load_sub<VEC, F32>(a, b, sp, mode, sc, xp, xq);
+  weights8<VEC, F32>(a, sp, mode, xp, xq, w);
+  wg_scan_incl(thread_sum(w), sh_wave, sh_incl);  // the same sub-chunk total as accept_decide_sum
   const int v0 = sc * kSub + 8 * tid;
   int lastp = -1;
 #pragma unroll
   for (int e = 0; e < 8; ++e)
     if (w[e] > 0.0) lastp = v0 + e;
-  if (!sh_past) {
+  if (!past) {
     // Thread k owns [base + incl[k-1], base + incl[k]): the intervals tile
-    // [base, base + total) exactly, so exactly one thread holds t.
-    const double lo = base + (tid ? sh_incl[0][tid - 1] : 0.0);
-    const double hi = base + sh_incl[0][tid];
+    // [base, base + total) exactly, so at most one thread holds t.
+    const double lo = base + (tid ? sh_incl[tid - 1] : 0.0);
+    const double hi = base + sh_incl[tid];
     if (lo <= t && t < hi) {
       double run = lo;
       int tok = lastp;
@@ -621,18 +685,19 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
       }
       found_tok = tok;
     }
-  } else if (lastp >= 0) {
-    atomicMax(&found_last, lastp);
   }
+  if (lastp >= 0) atomicMax(&found_last, lastp);
   __syncthreads();
   if (tid == 0) {
-    int tok = sh_past ? found_last : found_tok;
-    if (tok < 0 || tok == 0x7FFFFFFF) tok = min(a.V - 1, sc * kSub);
+    // No holder (t past the total, or a sub-chunk too small to move base):
+    // the last element with positive weight.
+    int tok = (!past && found_tok != 0x7FFFFFFF) ? found_tok : found_last;
+    if (tok < 0) tok = min(a.V - 1, sc * kSub);
     a.out_tokens[(size_t)b * a.N + sp.j] = tok;
     if (a.debug) {
       double* dbg = a.debug + ((size_t)b * (a.N + 1) + a.N) * 4;
       dbg[0] = sh_W;
-      dbg[1] = t;
+      dbg[1] = sh_t;
       dbg[2] = sp.u2;
       dbg[3] = (double)tok;
     }
@@ -646,6 +711,27 @@ int32_t launch_stats(const AccArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
+// Summing work-groups the chip keeps resident at once (queried once per
+// device and instantiation).
+template <bool VEC, bool F32>
+int64_t sum_slots() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cached[dev]) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, accept_decide_sum_kernel<VEC, F32>, 256, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
+}
+
 template <bool VEC, bool F32>
 int32_t launch_all(AccArgs a, int U1, hipStream_t s) {
   int32_t r;
@@ -656,8 +742,20 @@ int32_t launch_all(AccArgs a, int U1, hipStream_t s) {
     default: r = launch_stats<1, VEC, F32>(a, s); break;
   }
   if (r != IDLM_OK) return r;
-  // Greedy needs one decision work-group per sequence and no sampling.
-  if (a.greedy) a.S2 = 1;
+  if (a.greedy) {
+    // One decision work-group per sequence and no sampling.
+    a.spw = a.nsub;
+    a.S2 = 1;
+  } else {
+    // The fewest sub-chunks per work-group (up to kMaxSpw) that let the
+    // whole grid be resident at once.
+    const int64_t slots = sum_slots<VEC, F32>();
+    a.spw = 1;
+    while (a.spw < kMaxSpw && a.spw < a.nsub &&
+           (int64_t)a.B * ((a.nsub + a.spw - 1) / a.spw) > slots)
+      ++a.spw;
+    a.S2 = (a.nsub + a.spw - 1) / a.spw;
+  }
   const int64_t g2 = (int64_t)a.B * a.S2;
   hipLaunchKernelGGL((accept_decide_sum_kernel<VEC, F32>), dim3((unsigned)g2), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
@@ -696,8 +794,8 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.V = d.V;
   a.S1 = ap.S1;
   a.nsub = ap.nsub;
-  a.spw = ap.spw;
-  a.S2 = ap.S2;
+  a.spw = 1;  // set per launch
+  a.S2 = 1;
   a.f32 = d.logits_dtype == IDLM_F32;
   const bool vec = d.V % 8 == 0 && ((uintptr_t)lc % 16) == 0 &&
                    (lm == nullptr || ((uintptr_t)lm % 16) == 0);

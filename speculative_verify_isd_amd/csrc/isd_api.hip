@@ -63,10 +63,6 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
       break;
     }
   c.S1 = (int)ceil_div(d.V, (int64_t)kSub * c.U1);
-  // Sampling: up to 4 sub-chunks per work-group, aiming at ~2048 work-groups.
-  c.spw = (int)std::min<int64_t>(4, std::max<int64_t>(1, ceil_div((int64_t)c.nsub * std::max(d.B, 1), 2048)));
-  c.spw = std::min(c.spw, c.nsub);
-  c.S2 = (int)ceil_div(c.nsub, c.spw);
   // ---- workspace layout ----
   size_t o = 0;
   p->off_status = o;

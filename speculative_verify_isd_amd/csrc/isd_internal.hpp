@@ -17,7 +17,6 @@ namespace idlm {
 constexpr int kPage = 16;
 constexpr int kSub = 2048;  // acceptance sub-chunk: 256 threads x 8 elements
 constexpr int kMaxSubChunks = 1024;  // V <= kSub * kMaxSubChunks
-constexpr int kDecideStats = 1024;   // slice statistics a decision stages in LDS
 constexpr int kMaxWaves = 2048;   // streaming-attention waves resident at once (upper bound)
 constexpr int kMinRunPages = 8;   // shortest run of pages given to one wave-lane
 constexpr int kRingPages = RING_PAGES_DEFAULT;  // page buffers per attention wave (D = 128)
@@ -40,8 +39,6 @@ struct AcceptPlan {
   int nsub;       // kSub-element sub-chunks per row
   int U1;         // 16-byte vectors per thread in a stats work-group (1, 2, 4 or 8)
   int S1;         // stats work-groups per row: ceil(V / (kSub * U1))
-  int spw;        // sub-chunks per sampling work-group (1..4)
-  int S2;         // sampling work-groups per sequence
 };
 
 // Per-sequence hand-over from the ratio test to the sampler.
