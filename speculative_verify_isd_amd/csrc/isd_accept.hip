@@ -33,10 +33,14 @@
 //                      2048-element sub-chunks.  The first work-group writes
 //                      the kept prefix, the accept length and the plan (the
 //                      whole answer when T = 0).
-//   accept_select      grid B.  Wave 0 prefixes the sub-chunk sums, finds the
-//                      sub-chunk holding t = u' * sum(w); the work-group
-//                      recomputes that sub-chunk's weights bit for bit and
-//                      scans it to the smallest v whose running sum exceeds t.
+//   accept_select      grid B, one wave each.  The wave prefixes the
+//                      sub-chunk sums, finds the sub-chunk holding
+//                      t = u' * sum(w), recomputes that sub-chunk's weights
+//                      (each lane a contiguous run) and scans it to the
+//                      smallest v whose running sum exceeds t.  Where the
+//                      sub-chunk's own sum and its entry in the prefix differ
+//                      in the last bits, t is clamped into the sub-chunk, so
+//                      the pick is always an element with positive weight.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -95,6 +99,7 @@ struct AccArgs {
   SamplePlan* plan; // [B]
   double* subsum;   // [B][nsub]
   float* dlog;      // [B][R]: raw logit of the row's draft (rows that verify or proposed one)
+  double2* unif;    // [B][16]: (u_i, u'_i) for i = 0..K
   int B, N, K, R, V, S1, nsub, spw, S2, f32;  // spw, S2: chosen at launch
 };
 
@@ -164,30 +169,8 @@ __device__ inline void better(float& bv, int& bi, float v, int i) {
   }
 }
 
-// Inclusive scan of one double per thread over the work-group: thread t's
-// inclusive value lands in sh_incl[t].  Within a wave the scan takes lane
-// offsets 1, 2, ..., 32 in turn, so the value at lane 63 is the same sum, in
-// the same association, as the xor butterfly of wave_total(); across waves
-// the partial totals are added in wave order.
-__device__ inline void wg_scan_incl(double x, double* sh_wave, double* sh_incl) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) sh_wave[wave] = x;
-  __syncthreads();
-  double base = 0.0;
-  for (int w = 0; w < wave; ++w) base += sh_wave[w];
-  sh_incl[threadIdx.x] = base + x;
-  __syncthreads();
-}
-
-// The wave's total of x, read at lane 63: the xor butterfly over offsets 1,
-// 2, ..., 32 adds, at lane 63, exactly the operands the inclusive scan above
-// adds there (lane 63 - off holds the same partial sum in both), so the
-// totals agree bit for bit.
+// The wave's total of x in a fixed order (an xor butterfly); every call
+// with the same inputs gives the same bits, read at any one lane.
 __device__ inline double wave_total(double x) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
@@ -222,6 +205,12 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
   Logits8<VEC, F32> x[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) x[k] = load8<VEC, F32>(row, lo + k * kSub + 8 * tid, hi);
+  // The sequence's uniforms, drawn while the loads are in flight by the
+  // first slice of its first row: thread i <= K draws (u_i, u'_i).
+  if (rho == 0 && c == 0 && tid <= a.K) {
+    const U64x4 ph = philox4x64_10((uint64_t)tid, 0, 0, 0, a.seed, (uint64_t)b);
+    a.unif[(size_t)b * 16 + tid] = make_double2(top24(ph.w[0]), top24(ph.w[1]));
+  }
   if (xd >= lo && xd < hi && ((xd - lo) % kSub) / 8 == tid) {
     const int kd = (xd - lo) / kSub, ed = xd % 8;
     float val = 0.f;
@@ -326,9 +315,9 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
       lpf = a.dlog[(size_t)b * R + ic];
       lqf = a.dlog[(size_t)b * R + N + ic];
     }
-    // Philox while the loads are in flight: lane i draws (u_i, u'_i).
-    const U64x4 ph = philox4x64_10((uint64_t)lane, 0, 0, 0, a.seed, (uint64_t)b);
-    const double u = top24(ph.w[0]), u2 = top24(ph.w[1]);
+    // Lane i <= K: (u_i, u'_i), drawn by accept_stats.
+    const double2 uu = a.unif[(size_t)b * 16 + min(lane, K)];
+    const double u = uu.x, u2 = uu.y;
 
     // Row merge inside each L-lane group.  M (max) is exact in any order; S
     // is summed by a fixed butterfly and read from the group's lane 0.
@@ -437,7 +426,8 @@ __device__ void write_prefix(const AccArgs& a, int b, const SamplePlan& sp, int 
     a.out_len[b] = j + 1;
     for (int i = 0; i < a.K; ++i) {
       const int x = sh_ids[i];
-      if (x < -1 || x >= a.V) atomicOr(a.status, kBadDraft);
+      if (x < -1 || x >= a.V)  // system scope: XCD L2 caches are not coherent
+        __hip_atomic_fetch_or(a.status, kBadDraft, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       if (x < 0) break;
     }
   }
@@ -495,11 +485,10 @@ __device__ inline double thread_sum(const double w[8]) {
   return ts;
 }
 
-// This thread's 8 logits of sub-chunk sc in the p row (and q row, mode 0).
+// Logits v .. v+7 of the p row (and q row, mode 0).
 template <bool VEC, bool F32>
-__device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, int mode, int sc,
-                                Logits8<VEC, F32>& xp, Logits8<VEC, F32>& xq) {
-  const int v = sc * kSub + 8 * threadIdx.x;
+__device__ inline void load_sub_at(const AccArgs& a, int b, const SamplePlan& sp, int mode, int v,
+                                   Logits8<VEC, F32>& xp, Logits8<VEC, F32>& xq) {
   xp = load8<VEC, F32>(row_ptr(a, b, sp.row_p), v, a.V);
   if (mode == 0) {
     xq = load8<VEC, F32>(row_ptr(a, b, a.N + sp.row_q), v, a.V);
@@ -508,6 +497,13 @@ __device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, i
     for (int e = 0; e < Logits8<VEC, F32>::NW; ++e)
       xq.w[e] = Logits8<VEC, F32>::kPacked ? 0xFF80FF80u : 0xFF800000u;
   }
+}
+
+// This thread's 8 logits of sub-chunk sc (thread t: elements 8t .. 8t+7).
+template <bool VEC, bool F32>
+__device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, int mode, int sc,
+                                Logits8<VEC, F32>& xp, Logits8<VEC, F32>& xq) {
+  load_sub_at<VEC, F32>(a, b, sp, mode, sc * kSub + 8 * (int)threadIdx.x, xp, xq);
 }
 
 constexpr int kMaxSpw = 4;  // most sub-chunks one summing work-group takes
@@ -547,8 +543,6 @@ __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
     if (lane == 63) sh_wave[k][wave] = tot;
   }
   __syncthreads();
-  // The same total, in the same association, as thread 255's inclusive scan
-  // value in accept_select.
   if (tid < n)
     a.subsum[(size_t)b * a.nsub + sc_lo + tid] =
         ((sh_wave[tid][0] + sh_wave[tid][1]) + sh_wave[tid][2]) + sh_wave[tid][3];
@@ -619,40 +613,57 @@ __device__ void locate(const double* sh_sub, int nsub, double u2, double* sh_W, 
   }
 }
 
+constexpr int kSelPer = kSub / 64;  // elements per lane when one wave scans a sub-chunk
+
+// One lane's kSelPer consecutive logits of sub-chunk sc: lane l holds
+// elements sc * kSub + kSelPer * l + 0 .. kSelPer - 1, so lanes follow
+// vocabulary order.
 template <bool VEC, bool F32>
-__global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
-  __shared__ double sh_wave[4], sh_incl[256];
+__device__ inline void load_lane_run(const AccArgs& a, int b, const SamplePlan& sp, int mode,
+                                     int sc, Logits8<VEC, F32> (&xp)[kSelPer / 8],
+                                     Logits8<VEC, F32> (&xq)[kSelPer / 8]) {
+  const int v0 = sc * kSub + kSelPer * (int)threadIdx.x;
+#pragma unroll
+  for (int g = 0; g < kSelPer / 8; ++g) load_sub_at<VEC, F32>(a, b, sp, mode, v0 + 8 * g, xp[g], xq[g]);
+}
+
+// One wave per sequence.  Wave-level only: the sub-chunk sums are staged in
+// LDS, located by locate(), and the chosen sub-chunk is scanned with lane l
+// owning a contiguous run of kSelPer elements.
+template <bool VEC, bool F32>
+__global__ __launch_bounds__(64) void accept_select_kernel(AccArgs a) {
   __shared__ double sh_sub[kMaxSubChunks];
   __shared__ double sh_t, sh_base, sh_W;
   __shared__ int sh_sc, sh_past;
-  __shared__ int found_tok, found_last;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x;
   const int b = blockIdx.x;
   const double* subs = a.subsum + (size_t)b * a.nsub;
-  for (int i = tid; i < a.nsub; i += 256) sh_sub[i] = subs[i];
+  for (int i = lane; i < a.nsub; i += 64) sh_sub[i] = subs[i];
   const SamplePlan sp = a.plan[b];
   if (sp.mode == 2) return;
-  if (tid == 0) {
-    found_tok = 0x7FFFFFFF;
-    found_last = -1;
-  }
-  Logits8<VEC, F32> xp, xq;
-  double w[8];
+  constexpr int NG = kSelPer / 8;
+  Logits8<VEC, F32> xp[NG], xq[NG];
   int mode = sp.mode;
   __syncthreads();
-  if (tid < 64) locate(sh_sub, a.nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
+  locate(sh_sub, a.nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
   __syncthreads();
   if (!(sh_W > 0.0)) {
     // The residual vanished to rounding: fall back to p_j over the whole row.
     mode = 1;
     for (int sc = 0; sc < a.nsub; ++sc) {
-      load_sub<VEC, F32>(a, b, sp, 1, sc, xp, xq);
-      weights8<VEC, F32>(a, sp, 1, xp, xq, w);
-      wg_scan_incl(thread_sum(w), sh_wave, sh_incl);
-      if (tid == 0) sh_sub[sc] = sh_incl[255];
+      load_lane_run<VEC, F32>(a, b, sp, 1, sc, xp, xq);
+      double ls = 0.0;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        double w[8];
+        weights8<VEC, F32>(a, sp, 1, xp[g], xq[g], w);
+        ls += thread_sum(w);
+      }
+      const double tot = wave_total(ls);
+      if (lane == 63) sh_sub[sc] = tot;
     }
     __syncthreads();
-    if (tid < 64) locate(sh_sub, a.nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
+    locate(sh_sub, a.nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
     __syncthreads();
   }
   const double base = sh_base;
@@ -660,39 +671,60 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   // t sits in [base, base + sum of the sub-chunk) up to rounding at a
   // sub-chunk boundary; clamping it to base keeps it inside.
   const double t = fmax(sh_t, base);
-  load_sub<VEC, F32>(a, b, sp, mode, sc, xp, xq);
-  weights8<VEC, F32>(a, sp, mode, xp, xq, w);
-  wg_scan_incl(thread_sum(w), sh_wave, sh_incl);  // the same sub-chunk total as accept_decide_sum
-  const int v0 = sc * kSub + 8 * tid;
+  load_lane_run<VEC, F32>(a, b, sp, mode, sc, xp, xq);
+  const int v0 = sc * kSub + kSelPer * lane;
+  double ls = 0.0;
   int lastp = -1;
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (w[e] > 0.0) lastp = v0 + e;
-  if (!past) {
-    // Thread k owns [base + incl[k-1], base + incl[k]): the intervals tile
-    // [base, base + total) exactly, so at most one thread holds t.
-    const double lo = base + (tid ? sh_incl[tid - 1] : 0.0);
-    const double hi = base + sh_incl[tid];
-    if (lo <= t && t < hi) {
-      double run = lo;
-      int tok = lastp;
+  for (int g = 0; g < NG; ++g) {
+    double w[8];
+    weights8<VEC, F32>(a, sp, mode, xp[g], xq[g], w);
+    ls += thread_sum(w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (w[e] > 0.0) lastp = v0 + 8 * g + e;
+  }
+  // Lane l owns [base + ex_l, base + inc_l): consecutive lanes share their
+  // end points exactly, so at most one lane holds t.
+  double inc = ls;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  double ex = __shfl_up(inc, 1);
+  if (lane == 0) ex = 0.0;
+  const double lo = base + ex, hi = base + inc;
+  const bool holder = !past && lo <= t && t < hi;
+  int tok = -1;
+  if (holder) {
+    double run = lo;
+    tok = lastp;
+    bool done = false;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      double w[8];
+      weights8<VEC, F32>(a, sp, mode, xp[g], xq[g], w);
+#pragma unroll
       for (int e = 0; e < 8; ++e) {
         run += w[e];
-        if (run > t) {
-          tok = v0 + e;
-          break;
+        if (!done && run > t) {
+          tok = v0 + 8 * g + e;
+          done = true;
         }
       }
-      found_tok = tok;
     }
   }
-  if (lastp >= 0) atomicMax(&found_last, lastp);
-  __syncthreads();
-  if (tid == 0) {
+  const unsigned long long hm = __ballot(holder);
+  const unsigned long long pm = __ballot(lastp >= 0);
+  if (hm) {
+    tok = __shfl(tok, (int)__builtin_ctzll(hm));
+  } else {
     // No holder (t past the total, or a sub-chunk too small to move base):
     // the last element with positive weight.
-    int tok = (!past && found_tok != 0x7FFFFFFF) ? found_tok : found_last;
-    if (tok < 0) tok = min(a.V - 1, sc * kSub);
+    tok = pm ? __shfl(lastp, 63 - (int)__builtin_clzll(pm)) : min(a.V - 1, sc * kSub);
+  }
+  if (lane == 0) {
     a.out_tokens[(size_t)b * a.N + sp.j] = tok;
     if (a.debug) {
       double* dbg = a.debug + ((size_t)b * (a.N + 1) + a.N) * 4;
@@ -760,7 +792,7 @@ int32_t launch_all(AccArgs a, int U1, hipStream_t s) {
   hipLaunchKernelGGL((accept_decide_sum_kernel<VEC, F32>), dim3((unsigned)g2), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
   if (a.greedy) return IDLM_OK;
-  hipLaunchKernelGGL((accept_select_kernel<VEC, F32>), dim3((unsigned)a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((accept_select_kernel<VEC, F32>), dim3((unsigned)a.B), dim3(64), 0, s, a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
@@ -787,6 +819,7 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.plan = (SamplePlan*)(ws + p.off_splan);
   a.subsum = (double*)(ws + p.off_subsum);
   a.dlog = (float*)(ws + p.off_dlog);
+  a.unif = (double2*)(ws + p.off_unif);
   a.B = d.B;
   a.N = d.N;
   a.K = d.N - 1;

@@ -68,6 +68,7 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   p->off_status = o;
   o = align256(o + 4);
   // Streaming attention: two partial-state slots per wave-lane (bf16 path).
+  // Streaming attention: two partial-state slots per wave-lane (bf16 path).
   const size_t nslots = d.qkv_dtype == IDLM_BF16 ? (size_t)a.max_lanes * 2 : 0;
   p->off_attn_ml = o;
   o = align256(o + nslots * a.RGp * 8);
@@ -81,6 +82,8 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   o = align256(o + (size_t)d.B * c.nsub * 8);
   p->off_dlog = o;
   o = align256(o + (size_t)d.B * c.R * 4);
+  p->off_unif = o;
+  o = align256(o + (size_t)d.B * 16 * 16);
   p->total = o;
   return true;
 }

@@ -17,7 +17,8 @@
 //   of a pair is a segment.  A segment that covers its whole pair writes the
 //   final output; a partial one writes its softmax state (m, l, O) to one of
 //   the lane's two slots (a partial segment can only be a lane's first or
-//   last), and attn_merge_kernel combines the pieces in unit order.
+//   last), and attn_merge_kernel combines the pieces in unit order.  Run
+//   boundaries depend only on the sizes, so results do not depend on timing.
 //
 //   All R*G query rows of a pair share every K/V page, so each page is read
 //   once and reused across the query tile: a wave carries 32 query rows (two
@@ -60,8 +61,8 @@ struct AttnArgs {
   const int32_t* page_table;
   const int32_t* ctx_lens;
   void* out;
-  float* part_o;    // [nlanes][2][ROWS][D]
-  float2* part_ml;  // [nlanes][2][ROWS]
+  float* part_o;    // [2 * max_lanes][ROWS][D]: two slots per wave-lane
+  float2* part_ml;  // [2 * max_lanes][ROWS]
   int32_t* status;
   int B, R, Hq, Hkv, G, RG, D, max_pages, num_pages;
   int nlanes;       // wave-lanes of the streaming grid
@@ -74,7 +75,11 @@ __device__ inline u16 f32_to_bf16_rne(float f) {
   return (u16)(u >> 16);
 }
 
-__device__ inline void flag(int32_t* status, int32_t bit) { atomicOr(status, bit); }
+// Status bits may be set from any XCD; the XCDs' L2 caches are not coherent
+// with each other, so the OR is done at system scope (at memory).
+__device__ inline void flag(int32_t* status, int32_t bit) {
+  __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 // Context length clamped to [R, 16*max_pages]; `report` sets the status bit
 // when it had to clamp.
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rgrp = wave % WR;
+  const int rgrp = wave % WR;  // 32-row group of this wave
   const int wl = blockIdx.x * WK + wave / WR;  // this wave-lane
   bf16x8* qs = lds_q[wave];
   const int col = lane & 15, grp = lane >> 4;
@@ -287,35 +292,21 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
 
   const int64_t total = uni64(total_units_wave(a));
   const int64_t span = run_length(total, a.nlanes);
-  int64_t u = (int64_t)wl * span;
-  const int64_t uend = min(u + span, total);
-  if (u >= uend) return;
-
-  int64_t ub;
-  int ctx;
-  int b = locate_seq(a, u, &ub, &ctx);
-  b = uni(b);
-  ub = uni64(ub);
-  ctx = uni(ctx);
-  int np = pages_of(ctx);
-  int h = (int)((u - ub) / np);
 
   const u16* qb = (const u16*)a.q;
   const u16* kvb = (const u16*)a.kv;
   const size_t page_elems = (size_t)2 * a.Hkv * kPage * D;
   const size_t v_off = (size_t)a.Hkv * kPage * D;
   u16* outp = (u16*)a.out;
-  bool first_seg = true;
 
-  while (u < uend) {
-    const int64_t pair_start = ub + (int64_t)h * np;
-    const int p0 = (int)(u - pair_start);
-    const int p1 = (int)min<int64_t>(np, p0 + (uend - u));
-    const int nseg = p1 - p0;
-    const bool whole = (p0 == 0 && p1 == np);
+  float m[2], l[2];
+  f32x4 acc[2][ND];
+
+  // Streams pages [p0, p1) of pair (b, h) into (m, l, acc), starting from an
+  // empty state.
+  auto stream = [&](int b, int h, int ctx, int p0, int p1) __attribute__((always_inline)) {
     const size_t head_off = (size_t)h * kPage * D;
     const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
-
     // Query fragments (B operand of S^T = K Q^T): row = lane's column, eight
     // consecutive d per lane; k-step c covers d chunk 4c + grp.  Staged in
     // this wave's LDS slot; a wave's own LDS accesses stay in order.
@@ -335,116 +326,145 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
         qs[(rb * NC + c) * 64 + lane] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    float m[2] = {-INFINITY, -INFINITY};
-    float l[2] = {0.f, 0.f};
-    f32x4 acc[2][ND];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
+      m[rb] = -INFINITY;
+      l[rb] = 0.f;
 #pragma unroll
       for (int j = 0; j < ND; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // One page per step through a ring of kRing register buffers: kRing-1
-    // pages are in flight while one computes.  Every prefetch is issued
-    // unconditionally (so the compiler waits for exactly one buffer at a
-    // time); prefetches past the end re-read the last page (a cache hit) and
-    // their compute is fully masked.  The scheduling barriers keep each
-    // prefetch ahead of the compute it must overlap.
-    const int last = nseg - 1;
-    const int nrun = ((nseg + kRing - 1) / kRing) * kRing;
-    const int minpos = ctx - a.R;  // every row sees tokens up to here
-    auto issue = [&](PageFrag<D>& f, int st) {
-      const int pg = p0 + min(st, last);
-      int id = sload(pt, pg);
-      if ((unsigned)id >= (unsigned)a.num_pages) {
-        flag(a.status, kBadPage);
-        id = 0;
-      }
-      load_page<D>(f, kvb + (size_t)id * page_elems + head_off, v_off, lane);
-    };
-    auto run = [&](const PageFrag<D>& f, int st) {
-      const int t0 = (p0 + st) * kPage;
-      const bool has = st < nseg;
-      if (has && t0 + kPage - 1 <= minpos)
-        compute_page<D, false>(f, qs, lane, pos, t0 + 4 * grp, true, a.scale_log2, m, l, acc);
-      else
-        compute_page<D, true>(f, qs, lane, pos, t0 + 4 * grp, has, a.scale_log2, m, l, acc);
-    };
-    PageFrag<D> ring[kRing];
+    }
+    const int cnt = p1 - p0;
+    if (cnt > 0) {
+      // One page per step through a ring of kRing register buffers: kRing-1
+      // pages are in flight while one computes.  Every prefetch is issued
+      // unconditionally (so the compiler waits for exactly one buffer at a
+      // time); prefetches past the end re-read the last page (a cache hit)
+      // and their compute is fully masked.  The scheduling barriers keep
+      // each prefetch ahead of the compute it must overlap.
+      const int last = cnt - 1;
+      const int nrun = ((cnt + kRing - 1) / kRing) * kRing;
+      const int minpos = ctx - a.R;  // every row sees tokens up to here
+      auto issue = [&](PageFrag<D>& f, int st) __attribute__((always_inline)) {
+        const int pg = p0 + min(st, last);
+        int id = sload(pt, pg);
+        if ((unsigned)id >= (unsigned)a.num_pages) {
+          flag(a.status, kBadPage);
+          id = 0;
+        }
+        load_page<D>(f, kvb + (size_t)id * page_elems + head_off, v_off, lane);
+      };
+      auto run = [&](const PageFrag<D>& f, int st) __attribute__((always_inline)) {
+        const int t0 = (p0 + st) * kPage;
+        const bool has = st < cnt;
+        if (has && t0 + kPage - 1 <= minpos)
+          compute_page<D, false>(f, qs, lane, pos, t0 + 4 * grp, true, a.scale_log2, m, l, acc);
+        else
+          compute_page<D, true>(f, qs, lane, pos, t0 + 4 * grp, has, a.scale_log2, m, l, acc);
+      };
+      PageFrag<D> ring[kRing];
 #pragma unroll
-    for (int i = 0; i < kRing - 1; ++i) issue(ring[i], i);
-    for (int st = 0; st < nrun; st += kRing) {
+      for (int i = 0; i < kRing - 1; ++i) issue(ring[i], i);
+      for (int st = 0; st < nrun; st += kRing) {
 #pragma unroll
-      for (int i = 0; i < kRing; ++i) {
-        issue(ring[(i + kRing - 1) % kRing], st + i + kRing - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        run(ring[i], st + i);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < kRing; ++i) {
+          issue(ring[(i + kRing - 1) % kRing], st + i + kRing - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          run(ring[i], st + i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-
     // Row sums: every lane holds a partial over its tokens.
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       l[rb] += __shfl_xor(l[rb], 16);
       l[rb] += __shfl_xor(l[rb], 32);
     }
+  };
 
-    if (whole) {
-      // lane holds O^T[16j + 4grp + e][row col]: four consecutive d values.
+  // Final rows of pair (b, h): lane holds O^T[16j + 4grp + e][row col].
+  auto write_out = [&](int b, int h) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int i = rgrp * 32 + rb * 16 + col;
-        if (i < a.RG) {
-          const int r = i / a.G, g = i % a.G;
-          const float il = 1.f / l[rb];
-          u16* op = outp + (((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D + 4 * grp;
+    for (int rb = 0; rb < 2; ++rb) {
+      const int i = rgrp * 32 + rb * 16 + col;
+      if (i < a.RG) {
+        const int r = i / a.G, g = i % a.G;
+        const float il = 1.f / l[rb];
+        u16* op = outp + (((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D + 4 * grp;
 #pragma unroll
-          for (int j = 0; j < ND; ++j) {
-            const unsigned lo = f32_to_bf16_rne(acc[rb][j][0] * il) |
-                                ((unsigned)f32_to_bf16_rne(acc[rb][j][1] * il) << 16);
-            const unsigned hi = f32_to_bf16_rne(acc[rb][j][2] * il) |
-                                ((unsigned)f32_to_bf16_rne(acc[rb][j][3] * il) << 16);
-            *(uint2*)(op + 16 * j) = make_uint2(lo, hi);
-          }
+        for (int j = 0; j < ND; ++j) {
+          const unsigned lo = f32_to_bf16_rne(acc[rb][j][0] * il) |
+                              ((unsigned)f32_to_bf16_rne(acc[rb][j][1] * il) << 16);
+          const unsigned hi = f32_to_bf16_rne(acc[rb][j][2] * il) |
+                              ((unsigned)f32_to_bf16_rne(acc[rb][j][3] * il) << 16);
+          *(uint2*)(op + 16 * j) = make_uint2(lo, hi);
         }
       }
-    } else {
-      const size_t slot = (size_t)wl * 2 + (first_seg ? 0 : 1);
+    }
+  };
+  // Softmax state of a piece of a pair, for attn_merge_kernel.
+  auto write_part = [&](size_t slot) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int row = rgrp * 32 + rb * 16 + col;
-        float* po = a.part_o + (slot * ROWS + row) * D + 4 * grp;
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = rgrp * 32 + rb * 16 + col;
+      float* po = a.part_o + (slot * ROWS + row) * D + 4 * grp;
 #pragma unroll
-        for (int j = 0; j < ND; ++j)
-          *(float4*)(po + 16 * j) =
-              make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
-        if (grp == 0) a.part_ml[slot * ROWS + row] = make_float2(m[rb], l[rb]);
+      for (int j = 0; j < ND; ++j)
+        *(float4*)(po + 16 * j) =
+            make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
+      if (grp == 0) a.part_ml[slot * ROWS + row] = make_float2(m[rb], l[rb]);
+    }
+  };
+  // This lane's run, pair by pair; slots slot0 + 0 / + 1 hold its first /
+  // last piece when those are partial.
+  auto walk = [&](int64_t u, int64_t uend, size_t slot0) __attribute__((always_inline)) {
+    int64_t ub;
+    int ctx;
+    int b = locate_seq(a, u, &ub, &ctx);
+    b = uni(b);
+    ub = uni64(ub);
+    ctx = uni(ctx);
+    int np = pages_of(ctx);
+    int h = (int)((u - ub) / np);
+    bool first = true;
+    while (u < uend) {
+      const int64_t pair_start = ub + (int64_t)h * np;
+      const int p0 = (int)(u - pair_start);
+      const int p1 = (int)min<int64_t>(np, p0 + (uend - u));
+      const bool whole = (p0 == 0 && p1 == np);
+      stream(b, h, ctx, p0, p1);
+      if (whole)
+        write_out(b, h);
+      else
+        write_part(slot0 + (first ? 0 : 1));
+      u += p1 - p0;
+      first = false;
+      if (u < uend) {
+        if (++h == a.Hkv) {
+          h = 0;
+          ub += (int64_t)np * a.Hkv;
+          ++b;
+          ctx = uni(clamp_ctx(a, sload(a.ctx_lens, b), false));
+          np = pages_of(ctx);
+        }
       }
     }
+  };
 
-    // Next segment: the next KV head, or the next sequence.
-    u += nseg;
-    first_seg = false;
-    if (u < uend) {
-      if (++h == a.Hkv) {
-        h = 0;
-        ub += (int64_t)np * a.Hkv;
-        ++b;
-        ctx = uni(clamp_ctx(a, sload(a.ctx_lens, b), false));
-        np = pages_of(ctx);
-      }
-    }
-  }
+  const int64_t u = (int64_t)wl * span;
+  const int64_t uend = min(u + span, total);
+  if (u < uend) walk(u, uend, (size_t)wl * 2);
 }
 
-// Combines the partial segments of (b, h) pairs that were split across
-// wave-lanes, in unit order.  One work-group per pair; pairs written whole by
-// one lane exit at once.
+// Combines the pieces of (b, h) pairs that were split across wave-lane runs,
+// in unit order.  One work-group per pair; pairs written whole by one run
+// exit at once.
 template <int D, int WR>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * WR;
   constexpr int kMergeVec = (ROWS * D / 4 + 255) / 256;  // float4 outputs per thread
   constexpr int kMergeBlock = 16;                         // pieces per LDS block
+  constexpr int kBatch = kMergeVec < 16 ? 16 / kMergeVec : 1;  // pieces loaded together
   __shared__ int64_t sh_sum[4][2];
   __shared__ float sh_M[ROWS], sh_iL[ROWS];
   __shared__ float sh_f[kMergeBlock][ROWS];
@@ -477,12 +497,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int wa = (int)(start / span), wb = (int)((start + np - 1) / span);
   if (wa == wb) return;  // one lane held the whole pair and wrote the output
 
-  // Piece k comes from lane wa + k in slot 0, except that the first piece is
-  // in slot 1 when the pair starts inside lane wa's run.
+  // Piece k comes from lane wa + k: its run's first segment (slot + 0),
+  // except that the pair's first piece is lane wa's last segment (slot + 1)
+  // when the pair starts inside that lane's run.
   const int npieces = wb - wa + 1;
-  const int slot0 = (start == (int64_t)wa * span) ? 0 : 1;
-  auto slot_of = [&](int k) { return (size_t)(wa + k) * 2 + (k == 0 ? slot0 : 0); };
-  // Row maxima and normalisers over all pieces (independent loads, 4 at a time).
+  auto slot_of = [&](int k) -> size_t {
+    return (size_t)(wa + k) * 2 + ((k == 0 && start != (int64_t)wa * span) ? 1 : 0);
+  };
+  // Row maxima and normalisers over all pieces.
   if (tid < a.RG) {
     float M = -INFINITY;
 #pragma unroll 4
@@ -499,7 +521,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
   __syncthreads();
   // Each thread owns up to kMergeVec 4-wide d groups of the R*G x D output;
-  // pieces are folded in blocks whose scale factors sit in LDS.
+  // pieces are folded in blocks whose scale factors sit in LDS, kBatch
+  // pieces' loads at a time (clamped to a real piece, with factor 0).
   constexpr int D4 = D / 4;
   const int nvec = a.RG * D4;
   float4 O[kMergeVec];
@@ -507,25 +530,35 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   for (int e = 0; e < kMergeVec; ++e) O[e] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int kb = 0; kb < npieces; kb += kMergeBlock) {
     const int nk = min(kMergeBlock, npieces - kb);
-    for (int i = tid; i < nk * a.RG; i += 256) {
-      const int k = kb + i / a.RG, row = i % a.RG;
-      sh_f[i / a.RG][row] = exp2f(a.part_ml[slot_of(k) * ROWS + row].x - sh_M[row]) * sh_iL[row];
+    for (int i = tid; i < kMergeBlock * a.RG; i += 256) {
+      const int k = i / a.RG, row = i % a.RG;
+      sh_f[k][row] = k < nk ? exp2f(a.part_ml[slot_of(kb + k) * ROWS + row].x - sh_M[row]) * sh_iL[row]
+                            : 0.f;
     }
     __syncthreads();
-    for (int k = 0; k < nk; ++k) {
-      const float4* po = (const float4*)(a.part_o + slot_of(kb + k) * ROWS * D);
+    for (int k0 = 0; k0 < nk; k0 += kBatch) {
+      float4 v[kBatch][kMergeVec];
 #pragma unroll
-      for (int e = 0; e < kMergeVec; ++e) {
-        const int i = tid + 256 * e;
-        if (i < nvec) {
-          const float4 v = po[(i / D4) * D4 + i % D4];
-          const float f = sh_f[k][i / D4];
-          O[e].x += v.x * f;
-          O[e].y += v.y * f;
-          O[e].z += v.z * f;
-          O[e].w += v.w * f;
+      for (int t = 0; t < kBatch; ++t) {
+        const int k = min(k0 + t, nk - 1);
+        const float4* po = (const float4*)(a.part_o + slot_of(kb + k) * ROWS * D);
+#pragma unroll
+        for (int e = 0; e < kMergeVec; ++e) {
+          const int i = min(tid + 256 * e, nvec - 1);
+          v[t][e] = po[(i / D4) * D4 + i % D4];
         }
       }
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t)
+#pragma unroll
+        for (int e = 0; e < kMergeVec; ++e) {
+          const int i = min(tid + 256 * e, nvec - 1);
+          const float f = k0 + t < nk ? sh_f[k0 + t][i / D4] : 0.f;
+          O[e].x += v[t][e].x * f;
+          O[e].y += v[t][e].y * f;
+          O[e].z += v[t][e].z * f;
+          O[e].w += v[t][e].w * f;
+        }
     }
     __syncthreads();
   }

@@ -57,7 +57,7 @@ struct Plan {
   AttnPlan attn;
   AcceptPlan acc;
   size_t off_status, off_attn_ml, off_attn_o;
-  size_t off_splan, off_stats, off_subsum, off_dlog;
+  size_t off_splan, off_stats, off_subsum, off_dlog, off_unif;
   size_t total;
 };
 

@@ -173,10 +173,28 @@ def _picks(w, n, seed):
 def test_named_full_size(torch_cuda, name, sig):
     w = W.named_workload(name, sig)
     ds = run(w, torch_cuda)
-    picks = _picks(w, 6, 5)
+    # The extremes and random rows, plus one row of every sequence (so the
+    # tail of the unit list, which is scheduled dynamically, is covered).
+    rng = np.random.default_rng(11)
+    picks = _picks(w, 6, 5) + [(b, int(rng.integers(0, w.R)), int(rng.integers(0, w.Hq)))
+                               for b in range(w.B)]
     ref = oracle_attention_rows(w, picks)
     got = ds.out_f64()
     err = max(normwise_err(got[b, r, h], ref[n]) for n, (b, r, h) in enumerate(picks))
     print(f"[attn] sampled {picks} normwise err {err:.3e}", flush=True)
     assert err < ATTN_TOL["bf16"]
     check_accept(w, ds, allow_boundary=2)
+
+
+# ---------------------------------------------------------------------------
+# a large batch compared element by element: ~90k units over every wave-lane,
+# with pairs split across several lanes (one and two 32-row groups)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("Hq,D", [(8, 128), (64, 64)])
+def test_large_batch_full(torch_cuda, Hq, D):
+    rng = np.random.default_rng(23)
+    ctx = rng.integers(12000, 16384, size=12, endpoint=True)
+    w = small(f"large_hq{Hq}_d{D}", 12, 4, Hq, 8, D, 4096, ctx, seed=31)
+    ds = run(w, torch_cuda)
+    check_attn_full(w, ds)
+    check_accept(w, ds)
