@@ -10,10 +10,10 @@ logit perturbation sigma = 0.5, T = 1.
 
 Prints one JSON line with steps/s (``value``, from K whole steps between one
 pair of HIP events), committed and accepted-draft tokens/s, per-call times
-of isd_paged_attn and isd_accept from a second timed region with events
-between the two calls (all events on the launch stream), the attention
-roofline against 8 TB/s and the CPU oracle timed on a bounded sample of the
-same workload.
+(mean, median, p10, p90) of isd_paged_attn and isd_accept from a second
+timed region with events between the two calls (all events on the launch
+stream), the attention roofline against 8 TB/s and the CPU oracle timed on
+the same workload (whole batch, median of 3 single-threaded runs, ~15 s).
 """
 
 import os
@@ -74,33 +74,50 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, n_seq):
-    """Time the oracle on the first ``n_seq`` sequences and scale to the batch."""
+def cpu_baseline(w, n_seq, runs):
+    """Time the oracle (single thread) on the first ``n_seq`` sequences,
+    ``runs`` times, and scale the median to the whole batch."""
     from oracle.accept import isd_accept
     from oracle.attention import isd_attention
     from oracle.dtypes import to_f64
 
     sub = slice(0, n_seq)
     q = to_f64(w.q[sub], w.qkv_dtype).reshape(w.q[sub].shape)
-    t0 = time.perf_counter()
-    isd_attention(q, w.kv_pages, w.page_table[sub], w.ctx_lens[sub], w.N, w.Hkv, w.qkv_dtype)
-    t1 = time.perf_counter()
-    isd_accept(w.logits_clean[sub], w.logits_mask[sub], w.draft_tokens[sub], w.seed, w.T,
-               dtype=w.logits_dtype)
-    t2 = time.perf_counter()
+    t_attn, t_acc = [], []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        isd_attention(q, w.kv_pages, w.page_table[sub], w.ctx_lens[sub], w.N, w.Hkv, w.qkv_dtype)
+        t1 = time.perf_counter()
+        isd_accept(w.logits_clean[sub], w.logits_mask[sub], w.draft_tokens[sub], w.seed, w.T,
+                   dtype=w.logits_dtype)
+        t2 = time.perf_counter()
+        t_attn.append(t1 - t0)
+        t_acc.append(t2 - t1)
+    ta, tc = float(np.median(t_attn)), float(np.median(t_acc))
     tok_all = float(w.ctx_lens.sum())
     tok_sub = float(w.ctx_lens[sub].sum())
-    est = (t1 - t0) * tok_all / tok_sub + (t2 - t1) * w.B / n_seq
+    est = ta * tok_all / tok_sub + tc * w.B / n_seq
     return {
         "value": 1.0 / est,
         "unit": "ISD steps/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{n_seq} of {w.B} sequences ({int(tok_sub)} of {int(tok_all)} context "
-                  f"tokens): attention {t1 - t0:.2f} s scaled by context tokens, acceptance "
-                  f"{t2 - t1:.2f} s scaled by sequences; single thread, float64 numpy",
+        "sample": f"{n_seq} of {w.B} sequences ({int(tok_sub)} of {int(tok_all)} context tokens), "
+                  f"median of {runs} runs: attention {ta:.2f} s, acceptance {tc:.2f} s, scaled "
+                  f"by context tokens and by sequences to the batch; single thread, float64 "
+                  f"numpy; {os.cpu_count()} host CPUs, {_cpu_model()}",
         "step_seconds_estimated": est,
     }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def main():
@@ -110,7 +127,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c64")
     ap.add_argument("--sigma-index", type=int, default=1)
-    ap.add_argument("--cpu-sample", type=int, default=4, help="sequences timed on the oracle")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="sequences timed on the oracle (0: the whole batch)")
+    ap.add_argument("--cpu-runs", type=int, default=3, help="oracle runs (median)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
@@ -171,8 +190,14 @@ def main():
         ds.accept(debug=False)
         ev[k][2].record(stream)
     torch.cuda.synchronize()
-    attn_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]))
-    acc_ms = float(np.mean([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]))
+    attn_t = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)])
+    acc_t = np.array([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)])
+    attn_ms = float(attn_t.mean())
+    acc_ms = float(acc_t.mean())
+
+    def spread(t):
+        return {"median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+                "p90_ms": float(np.percentile(t, 90))}
 
     lens = ds.lens.cpu().numpy()
     kp = (w.draft_tokens >= 0).sum(axis=1) if w.N > 1 else np.zeros(w.B, dtype=np.int64)
@@ -210,17 +235,18 @@ def main():
         "accepted_draft_tok_per_s": (committed - w.B) * 1000.0 / ms_per_step,
         "mean_accept_len": committed / w.B,
         "kernels": {
-            "isd_paged_attn": {"ms": attn_ms, "algorithmic_bytes": a_bytes, "GB/s": attn_gbs,
-                               "frac_of_8TB/s": attn_gbs / HBM_PEAK_GBS},
-            "isd_accept": {"ms": acc_ms, "algorithmic_bytes": c_bytes, "GB/s": acc_gbs,
-                           "frac_of_8TB/s": acc_gbs / HBM_PEAK_GBS},
+            "isd_paged_attn": {"ms": attn_ms, **spread(attn_t), "algorithmic_bytes": a_bytes,
+                               "GB/s": attn_gbs, "frac_of_8TB/s": attn_gbs / HBM_PEAK_GBS},
+            "isd_accept": {"ms": acc_ms, **spread(acc_t), "algorithmic_bytes": c_bytes,
+                           "GB/s": acc_gbs, "frac_of_8TB/s": acc_gbs / HBM_PEAK_GBS},
         },
         "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic},
         "host_wall_s": wall,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+        n = args.cpu_sample if 0 < args.cpu_sample <= w.B else w.B
+        res["cpu_baseline"] = cpu_baseline(w, n, max(1, args.cpu_runs))
     print(json.dumps(res), flush=True)
 
 
