@@ -131,6 +131,8 @@ def main():
                     help="sequences timed on the oracle (0: the whole batch)")
     ap.add_argument("--cpu-runs", type=int, default=3, help="oracle runs (median)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time K replays of one step captured in a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -199,6 +201,30 @@ def main():
         return {"median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
                 "p90_ms": float(np.percentile(t, 90))}
 
+    graph_ms = None
+    if args.graph:
+        # One step captured in a graph (kernel nodes only), replayed K times.
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            ds.step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ds.step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(K):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+
     lens = ds.lens.cpu().numpy()
     kp = (w.draft_tokens >= 0).sum(axis=1) if w.N > 1 else np.zeros(w.B, dtype=np.int64)
     committed = int(lens.sum())
@@ -244,6 +270,8 @@ def main():
                      "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic},
         "host_wall_s": wall,
     }
+    if graph_ms is not None:
+        res["graph"] = {"ms_per_step": graph_ms, "steps_per_s": 1000.0 / graph_ms}
     if not args.no_cpu_baseline:
         n = args.cpu_sample if 0 < args.cpu_sample <= w.B else w.B
         res["cpu_baseline"] = cpu_baseline(w, n, max(1, args.cpu_runs))

@@ -27,7 +27,10 @@
  *   allocates nothing; per-call scratch lives in the caller's workspace.
  * - Everything is enqueued on `stream` (a hipStream_t passed as void*;
  *   NULL = the default stream) and returns without synchronising, except
- *   idlm_isd_read_status.
+ *   idlm_isd_read_status.  The enqueued work is kernel launches only (no
+ *   memset or copy nodes, no host synchronisation, no allocation), so every
+ *   entry point but idlm_isd_read_status can be captured into a HIP graph
+ *   and replayed; scalar arguments (seed, T) are fixed at capture.
  * - A nonzero return is an idlm_status; nothing was enqueued when a call
  *   fails host-side validation.  Host validation needs no GPU.
  * - Bad *device data* (a page id outside [0, num_pages), a context length
