@@ -110,6 +110,60 @@ def cpu_baseline(w, n_seq, runs):
     }
 
 
+def time_kv(ds, w, K):
+    """Per-call times of idlm_isd_kv_append (the step's R rows into the
+    cache) and idlm_isd_kv_rollback (back to the accepted prefix) on the
+    workload's own cache: contexts ctx_lens - R before the append, the pool's
+    unused pages as the free stack, state restored before every call (outside
+    the events).  An attention call precedes each timed pair so the launch
+    queue stays ahead of the GPU and the events see GPU time only."""
+    import torch
+
+    from speculative_verify_isd_amd import lib as L
+
+    R = 2 * w.N - 1
+    in_use = np.zeros(w.kv_pages.shape[0], dtype=bool)
+    in_use[w.page_table[w.page_table >= 0]] = True
+    free = np.nonzero(~in_use)[0].astype(np.int32)
+    stack0 = torch.full((w.kv_pages.shape[0],), -1, dtype=torch.int32, device="cuda")
+    stack0[: len(free)] = torch.from_numpy(free).cuda()
+    table0 = ds.page_table.clone()
+    ctx0 = ds.ctx_lens - R
+    rng = np.random.default_rng(1)
+    kdt = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
+    k_new = torch.from_numpy(rng.standard_normal((w.B, R, w.Hkv, w.D)).astype(np.float32)).to(
+        "cuda", kdt)
+    v_new = k_new.flip(0).contiguous()
+    table, stack = table0.clone(), stack0.clone()
+    count = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ctx1 = torch.empty_like(ctx0)
+    ctx2 = torch.empty_like(ctx0)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for k in range(K + 3):
+        ds.attn()  # untimed: keeps the GPU busy while the host enqueues the timed calls
+        table.copy_(table0)
+        stack.copy_(stack0)
+        count.fill_(len(free))
+        e = ev[k - 3] if k >= 3 else None
+        if e:
+            e[0].record()
+        L.idlm_isd_kv_append(ds.dims, k_new, v_new, ctx0, ctx1, ds.kv, table, stack, count, ds.ws)
+        if e:
+            e[1].record()
+        L.idlm_isd_kv_rollback(ds.dims, ctx1, ds.lens, ctx2, table, stack, count, ds.ws)
+        if e:
+            e[2].record()
+    torch.cuda.synchronize()
+    assert L.idlm_isd_read_status(ds.ws) == 0
+    app = float(np.mean([x[0].elapsed_time(x[1]) for x in ev])) * 1e3
+    rb = float(np.mean([x[1].elapsed_time(x[2]) for x in ev])) * 1e3
+    es = 2 if w.qkv_dtype == "bf16" else 4
+    nbytes = 2 * (2 * w.B * R * w.Hkv * w.D * es)  # K and V rows read, then written
+    return {"kv_append": {"us": app, "algorithmic_bytes": nbytes,
+                          "GB/s": nbytes / (app * 1e-6) / 1e9},
+            "kv_rollback": {"us": rb}}
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -225,6 +279,8 @@ def main():
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / K
 
+    kv = time_kv(ds, w, K)
+
     lens = ds.lens.cpu().numpy()
     kp = (w.draft_tokens >= 0).sum(axis=1) if w.N > 1 else np.zeros(w.B, dtype=np.int64)
     committed = int(lens.sum())
@@ -270,6 +326,7 @@ def main():
                      "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic},
         "host_wall_s": wall,
     }
+    res["next_rows"] = kv
     if graph_ms is not None:
         res["graph"] = {"ms_per_step": graph_ms, "steps_per_s": 1000.0 / graph_ms}
     if not args.no_cpu_baseline:

@@ -19,6 +19,9 @@
  *      truncated there ("Introspective Diffusion Language Models", section
  *      "Inference & ISD"; GeekNews summary, section "Inference & ISD").
  *   3. idlm_isd_step: 1 then 2 on one stream.
+ *   4. idlm_isd_kv_append / idlm_isd_kv_rollback: the cache writes around a
+ *      step (new rows in before attention, back to the accepted prefix
+ *      after acceptance).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -165,6 +168,48 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
                       const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
                       int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
                       void* workspace, size_t ws_bytes, void* stream);
+
+/* KV append, before attention.  Writes the R step rows' keys and values into
+ * the paged cache at positions ctx_before[b] .. ctx_before[b]+R-1 (the cache
+ * is paged and serves continuous batching: "Introspective Diffusion Language
+ * Models", section "Serving (SGLang)").
+ *   k_new, v_new [device] [B][R][Hkv][D] qkv_dtype (keys rotated already)
+ *   ctx_before   [device] int32 [B]: tokens already cached
+ *   ctx_after    [device] int32 [B], written: ctx_before + R (the ctx_lens
+ *                of idlm_isd_paged_attn); may be the same array as ctx_before
+ *   kv_pages     [device] pool, layout above; rows written in place
+ *   page_table   [device] int32 [B][max_pages]; entries of new pages written
+ *   free_pages   [device] int32 [num_pages]: a stack of free page ids, the
+ *                first *free_count entries valid
+ *   free_count   [device] int32 scalar, updated
+ * The call takes T pages in total, the top T stack entries, sequence by
+ * sequence in batch order and each sequence's pages in page order (no
+ * atomics: the same inputs give the same assignment).  Device-data errors
+ * (read_status): a ctx_before outside [0, 16*max_pages - R] (that sequence is
+ * left unchanged), too few free pages or a free-list id outside
+ * [0, num_pages) (the whole call is left unchanged). */
+int32_t idlm_isd_kv_append(const idlm_isd_dims* d, const void* k_new, const void* v_new,
+                           const int32_t* ctx_before, int32_t* ctx_after, void* kv_pages,
+                           int32_t* page_table, int32_t* free_pages, int32_t* free_count,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* KV rollback, after acceptance.  Only the anchor and the accepted drafts
+ * stay context (the first rejection ends the kept prefix: "Introspective
+ * Diffusion Language Models", section "Inference & ISD"), so sequence b keeps
+ * ctx_lens[b] - R + accept_len[b] tokens; page-table entries past that are
+ * set to -1 and their pages pushed on the free stack in batch order, page
+ * order.  Freed pages keep their stale contents.
+ *   ctx_lens   [device] int32 [B]: the step's context (R rows included)
+ *   accept_len [device] int32 [B]: idlm_isd_accept's output, in [1, R]
+ *              (clamped otherwise and reported)
+ *   ctx_after  [device] int32 [B], written; may be the same array as ctx_lens
+ *   page_table, free_pages, free_count as for idlm_isd_kv_append
+ * Device-data errors: a ctx_lens outside [R, 16*max_pages] (sequence left
+ * unchanged), a stack overflow past num_pages (call left unchanged). */
+int32_t idlm_isd_kv_rollback(const idlm_isd_dims* d, const int32_t* ctx_lens,
+                             const int32_t* accept_len, int32_t* ctx_after, int32_t* page_table,
+                             int32_t* free_pages, int32_t* free_count, void* workspace,
+                             size_t ws_bytes, void* stream);
 
 /* Synchronise `stream`, then copy the workspace's sticky device status into
  * *host_code (IDLM_OK or IDLM_ERR_DEVICE_DATA).  Cleared only by

@@ -27,6 +27,8 @@ attention  Strictly causal GQA attention of the 2N-1 step rows over the paged
 accept     The p/q acceptance loop, residual resampling and truncation.
 tpf        The tokens-per-forward closed form and the two-state decode chain
            it is the stationary mean of.
+kv_cache   KV-cache append (before attention) and rollback to the accepted
+           prefix (after acceptance), with a free-list page stack.
 dtypes     Exact widening of bfloat16 bit patterns.
 
 Every function listed has at least one pin in ``tests/`` that ties it to

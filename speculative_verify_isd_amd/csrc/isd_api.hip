@@ -84,6 +84,8 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   o = align256(o + (size_t)d.B * c.R * 4);
   p->off_unif = o;
   o = align256(o + (size_t)d.B * 16 * 16);
+  p->off_kv_valid = o;
+  o = align256(o + (size_t)d.B);
   p->total = o;
   return true;
 }
@@ -188,6 +190,39 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
   if (r != IDLM_OK) return r;
   return launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
                        out_accept_len, nullptr, (char*)workspace, s);
+}
+
+int32_t idlm_isd_kv_append(const idlm_isd_dims* d, const void* k_new, const void* v_new,
+                           const int32_t* ctx_before, int32_t* ctx_after, void* kv_pages,
+                           int32_t* page_table, int32_t* free_pages, int32_t* free_count,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  int32_t r = check_dims(d);
+  if (r != IDLM_OK) return r;
+  Plan p;
+  make_plan(*d, &p);
+  if ((r = check_ws(p, workspace, ws_bytes)) != IDLM_OK) return r;
+  if (d->B == 0) return IDLM_OK;
+  if (!k_new || !v_new || !ctx_before || !ctx_after || !kv_pages || !page_table || !free_pages ||
+      !free_count)
+    return IDLM_ERR_NULL;
+  return launch_kv_append(*d, p, k_new, v_new, ctx_before, ctx_after, kv_pages, page_table,
+                          free_pages, free_count, (char*)workspace, (hipStream_t)stream);
+}
+
+int32_t idlm_isd_kv_rollback(const idlm_isd_dims* d, const int32_t* ctx_lens,
+                             const int32_t* accept_len, int32_t* ctx_after, int32_t* page_table,
+                             int32_t* free_pages, int32_t* free_count, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  int32_t r = check_dims(d);
+  if (r != IDLM_OK) return r;
+  Plan p;
+  make_plan(*d, &p);
+  if ((r = check_ws(p, workspace, ws_bytes)) != IDLM_OK) return r;
+  if (d->B == 0) return IDLM_OK;
+  if (!ctx_lens || !accept_len || !ctx_after || !page_table || !free_pages || !free_count)
+    return IDLM_ERR_NULL;
+  return launch_kv_rollback(*d, p, ctx_lens, accept_len, ctx_after, page_table, free_pages,
+                            free_count, (char*)workspace, (hipStream_t)stream);
 }
 
 int32_t idlm_isd_read_status(const void* workspace, void* stream, int32_t* host_code) {

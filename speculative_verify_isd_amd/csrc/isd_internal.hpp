@@ -22,7 +22,7 @@ constexpr int kMinRunPages = 8;   // shortest run of pages given to one wave-lan
 constexpr int kRingPages = RING_PAGES_DEFAULT;  // page buffers per attention wave (D = 128)
 
 // Sticky device status bits (workspace word 0).
-enum : int32_t { kBadPage = 1, kBadCtx = 2, kBadDraft = 4 };
+enum : int32_t { kBadPage = 1, kBadCtx = 2, kBadDraft = 4, kFreeList = 8, kBadLen = 16 };
 
 // Attention sizes derived from the dims.
 struct AttnPlan {
@@ -58,6 +58,7 @@ struct Plan {
   AcceptPlan acc;
   size_t off_status, off_attn_ml, off_attn_o;
   size_t off_splan, off_stats, off_subsum, off_dlog, off_unif;
+  size_t off_kv_valid;
   size_t total;
 };
 
@@ -72,5 +73,14 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
                       int32_t* out_len, double* out_debug, char* ws, hipStream_t s);
 
 int32_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
+
+int32_t launch_kv_append(const idlm_isd_dims& d, const Plan& p, const void* k_new,
+                         const void* v_new, const int32_t* ctx_before, int32_t* ctx_after,
+                         void* kv_pages, int32_t* page_table, int32_t* free_pages,
+                         int32_t* free_count, char* ws, hipStream_t s);
+
+int32_t launch_kv_rollback(const idlm_isd_dims& d, const Plan& p, const int32_t* ctx_lens,
+                           const int32_t* accept_len, int32_t* ctx_after, int32_t* page_table,
+                           int32_t* free_pages, int32_t* free_count, char* ws, hipStream_t s);
 
 }  // namespace idlm

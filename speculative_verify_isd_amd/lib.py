@@ -37,6 +37,8 @@ ENTRY_POINTS = (
     "idlm_isd_paged_attn",
     "idlm_isd_accept",
     "idlm_isd_step",
+    "idlm_isd_kv_append",
+    "idlm_isd_kv_rollback",
     "idlm_isd_read_status",
     "idlm_isd_strerror",
 )
@@ -85,6 +87,8 @@ def load():
         "idlm_isd_paged_attn": (i32, [D, P, P, P, P, P, P, sz, P]),
         "idlm_isd_accept": (i32, [D, P, P, P, u64, f32, P, P, P, P, sz, P]),
         "idlm_isd_step": (i32, [D, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, sz, P]),
+        "idlm_isd_kv_append": (i32, [D, P, P, P, P, P, P, P, P, P, sz, P]),
+        "idlm_isd_kv_rollback": (i32, [D, P, P, P, P, P, P, P, sz, P]),
         "idlm_isd_read_status": (i32, [P, P, ctypes.POINTER(i32)]),
         "idlm_isd_strerror": (ctypes.c_char_p, [i32]),
     }
@@ -207,6 +211,29 @@ def idlm_isd_step(dims, q, kv_pages, page_table, ctx_lens, logits_clean, logits_
         _ptr(out_tokens, _i32(), "out_tokens"), _ptr(out_accept_len, _i32(), "out_accept_len"),
         _ptr(attn_out, fq, "attn_out"), _ptr(ws, (torch.uint8,), "workspace"), ws.numel(),
         _stream()), "idlm_isd_step")
+
+
+def idlm_isd_kv_append(dims, k_new, v_new, ctx_before, ctx_after, kv_pages, page_table,
+                       free_pages, free_count, ws):
+    dt = _fdt(dims.qkv_dtype)
+    _check(load().idlm_isd_kv_append(
+        ctypes.byref(dims), _ptr(k_new, dt, "k_new"), _ptr(v_new, dt, "v_new"),
+        _ptr(ctx_before, _i32(), "ctx_before"), _ptr(ctx_after, _i32(), "ctx_after"),
+        _ptr(kv_pages, dt, "kv_pages"), _ptr(page_table, _i32(), "page_table"),
+        _ptr(free_pages, _i32(), "free_pages"), _ptr(free_count, _i32(), "free_count"),
+        _ptr(ws, (_torch().uint8,), "workspace"), ctypes.c_size_t(ws.numel()), _stream()),
+        "idlm_isd_kv_append")
+
+
+def idlm_isd_kv_rollback(dims, ctx_lens, accept_len, ctx_after, page_table, free_pages,
+                         free_count, ws):
+    _check(load().idlm_isd_kv_rollback(
+        ctypes.byref(dims), _ptr(ctx_lens, _i32(), "ctx_lens"),
+        _ptr(accept_len, _i32(), "accept_len"), _ptr(ctx_after, _i32(), "ctx_after"),
+        _ptr(page_table, _i32(), "page_table"), _ptr(free_pages, _i32(), "free_pages"),
+        _ptr(free_count, _i32(), "free_count"), _ptr(ws, (_torch().uint8,), "workspace"),
+        ctypes.c_size_t(ws.numel()), _stream()),
+        "idlm_isd_kv_rollback")
 
 
 def idlm_isd_read_status(ws):

@@ -146,6 +146,26 @@ def make_pages(rng, ctx_lens, max_pages, Hkv, D, dtype, permute=True, slack=1.1,
     return pool, table
 
 
+def make_cache_state(rng, ctx_before, max_pages, Hkv, D, R, dtype, spare):
+    """A cache before a step's KV append: pool, page table for ``ctx_before``,
+    a free-page stack (the unused pool pages in random order, int32
+    [P] with the first ``free_count`` valid) and the step's new K/V rows
+    [B][R][Hkv][D].  ``spare`` extra pages beyond what the contexts use."""
+    ctx_before = np.asarray(ctx_before, dtype=np.int32)
+    used = int(sum((int(c) + PAGE - 1) // PAGE for c in ctx_before))
+    pool, table = make_pages(rng, ctx_before, max_pages, Hkv, D, dtype, permute=True, slack=1.0,
+                             min_pages=used + spare)
+    in_use = np.zeros(pool.shape[0], dtype=bool)
+    in_use[table[table >= 0]] = True
+    free = rng.permutation(np.nonzero(~in_use)[0]).astype(np.int32)
+    stack = np.full(pool.shape[0], -1, dtype=np.int32)
+    stack[:len(free)] = free
+    B = len(ctx_before)
+    k_new = _normal_store(rng, (B, R, Hkv, D), 1.0, dtype)
+    v_new = _normal_store(rng, (B, R, Hkv, D), 1.0, dtype)
+    return pool, table, stack, len(free), k_new, v_new
+
+
 def sample_drafts(rng, logits_mask, dtype, T, n_drafts=None):
     """Draft tokens drawn from softmax(mask / T) by Gumbel-max (argmax at T = 0).
 

@@ -120,3 +120,22 @@ def test_strerror(so):
         s = L.strerror(code)
         assert isinstance(s, str) and s
     assert L.strerror(99) == "unknown status"
+
+
+def test_kv_append_rejects_before_launch(so):
+    d = good()
+    n = L.idlm_isd_workspace_bytes(d)
+    fake = ctypes.c_void_p(1 << 20)
+    a = [fake] * 8
+    assert so.idlm_isd_kv_append(ctypes.byref(good(D=96)), *a, fake, n, None) == 3
+    assert so.idlm_isd_kv_append(ctypes.byref(d), None, *a[1:], fake, n, None) == 1
+    assert so.idlm_isd_kv_append(ctypes.byref(d), *a[:7], None, fake, n, None) == 1
+    assert so.idlm_isd_kv_append(ctypes.byref(d), *a, fake, n - 256, None) == 5
+    r = [fake] * 6
+    assert so.idlm_isd_kv_rollback(ctypes.byref(d), None, *r[1:], fake, n, None) == 1
+    assert so.idlm_isd_kv_rollback(ctypes.byref(d), *r, None, n, None) == 1
+    assert so.idlm_isd_kv_rollback(ctypes.byref(good(N=0)), *r, fake, n, None) == 2
+    e = good(B=0)
+    ne = L.idlm_isd_workspace_bytes(e)
+    assert so.idlm_isd_kv_append(ctypes.byref(e), *([None] * 8), fake, ne, None) == 0
+    assert so.idlm_isd_kv_rollback(ctypes.byref(e), *([None] * 6), fake, ne, None) == 0

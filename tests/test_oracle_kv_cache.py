@@ -1,0 +1,118 @@
+"""Pins of oracle.kv_cache: append then gather returns the new rows after
+the old context; rollback then gather returns the kept prefix; the pages in
+use plus the free pages are always the same set; the stack order."""
+
+import numpy as np
+
+from oracle.attention import gather_kv
+from oracle.dtypes import to_f64
+from oracle.kv_cache import kv_append, kv_rollback, pages_of
+from speculative_verify_isd_amd import workloads as W
+
+
+def _cache(rng, B, Hkv, D, ctx, dtype, spare):
+    """A pool with the given contexts, spare free pages on a stack."""
+    max_pages = int(pages_of(max(ctx) + 40))
+    used = int(pages_of(np.asarray(ctx)).sum())
+    P = used + spare
+    pool, table = W.make_pages(rng, np.asarray(ctx, dtype=np.int32), max_pages, Hkv, D, dtype,
+                               permute=True, slack=1.0)
+    # make_pages sizes the pool for the contexts; append spare pages
+    extra = np.zeros((P - pool.shape[0],) + pool.shape[1:], dtype=pool.dtype)
+    pool = np.concatenate([pool, extra])
+    in_use = set(int(v) for v in table.ravel() if v >= 0)
+    free = np.array([p for p in rng.permutation(P) if p not in in_use], dtype=np.int32)
+    return pool, table, free
+
+
+def _rows(rng, B, R, Hkv, D, dtype):
+    a = rng.standard_normal((B, R, Hkv, D)).astype(np.float32)
+    return W.f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def _page_set(table, free, count):
+    s = [int(v) for v in table.ravel() if v >= 0] + [int(v) for v in free[:count]]
+    return sorted(s)
+
+
+def test_append_then_gather():
+    rng = np.random.default_rng(3)
+    for dtype, D in (("bf16", 128), ("f32", 64)):
+        B, R, Hkv = 4, 7, 2
+        ctx = [0, 5, 16, 30]
+        pool, table, free = _cache(rng, B, Hkv, D, ctx, dtype, spare=12)
+        k_new, v_new = _rows(rng, B, R, Hkv, D, dtype), _rows(rng, B, R, Hkv, D, dtype)
+        before = {(b, h): gather_kv(pool, dtype, table[b], ctx[b], h, D)
+                  for b in range(B) for h in range(Hkv)}
+        pool2, table2, ctx2, cnt, err = kv_append(pool, table, ctx, k_new, v_new, free, len(free),
+                                                  dtype)
+        assert not err
+        assert list(ctx2) == [c + R for c in ctx]
+        for b in range(B):
+            for h in range(Hkv):
+                K, V = gather_kv(pool2, dtype, table2[b], int(ctx2[b]), h, D)
+                K0, V0 = before[(b, h)]
+                assert np.array_equal(K[:ctx[b]], K0) and np.array_equal(V[:ctx[b]], V0)
+                kn = to_f64(k_new[b, :, h], dtype).reshape(R, D)
+                vn = to_f64(v_new[b, :, h], dtype).reshape(R, D)
+                assert np.array_equal(K[ctx[b]:], kn) and np.array_equal(V[ctx[b]:], vn)
+        # pages: the stack top, in sequence order, each sequence's pages in order
+        need = pages_of(np.asarray(ctx) + R) - pages_of(np.asarray(ctx))
+        got = [int(table2[b, int(pages_of(ctx[b])) + i]) for b in range(B) for i in range(need[b])]
+        assert got == [int(v) for v in free[cnt:len(free)]]
+        assert _page_set(table2, free, cnt) == _page_set(table, free, len(free))
+
+
+def test_rollback_keeps_prefix_and_conserves_pages():
+    rng = np.random.default_rng(4)
+    B, R, Hkv, D, dtype = 5, 7, 2, 64, "bf16"
+    ctx0 = [0, 9, 15, 16, 40]
+    pool, table, free = _cache(rng, B, Hkv, D, ctx0, dtype, spare=20)
+    k_new, v_new = _rows(rng, B, R, Hkv, D, dtype), _rows(rng, B, R, Hkv, D, dtype)
+    pool, table, ctx, cnt, err = kv_append(pool, table, ctx0, k_new, v_new, free, len(free), dtype)
+    assert not err
+    acc = np.array([1, 4, 2, 7, 3])
+    table2, ctx2, free2, cnt2, err = kv_rollback(table, ctx, acc, R, free, cnt)
+    assert not err
+    assert list(ctx2) == [c + a for c, a in zip(ctx0, acc)]
+    for b in range(B):
+        assert (table2[b, int(pages_of(ctx2[b])):] == -1).all()
+        for h in range(Hkv):
+            K, V = gather_kv(pool, dtype, table2[b], int(ctx2[b]), h, D)
+            Kf, Vf = gather_kv(pool, dtype, table[b], int(ctx[b]), h, D)
+            assert np.array_equal(K, Kf[: ctx2[b]]) and np.array_equal(V, Vf[: ctx2[b]])
+    assert _page_set(table2, free2, cnt2) == _page_set(table, free, cnt)
+    # freed pages land on the stack in sequence order, page order
+    freed = [int(table[b, p]) for b in range(B)
+             for p in range(int(pages_of(ctx2[b])), int(pages_of(ctx[b])))]
+    assert [int(v) for v in free2[cnt:cnt2]] == freed
+
+
+def test_append_errors_change_nothing():
+    rng = np.random.default_rng(5)
+    B, R, Hkv, D, dtype = 3, 7, 1, 64, "bf16"
+    ctx = [3, 14, 20]
+    pool, table, free = _cache(rng, B, Hkv, D, ctx, dtype, spare=2)
+    k_new, v_new = _rows(rng, B, R, Hkv, D, dtype), _rows(rng, B, R, Hkv, D, dtype)
+    # needs: 1 (3->10 stays in page 0? pages_of(10)=1, pages_of(3)=1 -> 0), ...
+    need = int((pages_of(np.asarray(ctx) + R) - pages_of(np.asarray(ctx))).sum())
+    pool2, table2, ctx2, cnt, err = kv_append(pool, table, ctx, k_new, v_new, free, need - 1, dtype)
+    assert err == {"no_pages"}
+    assert np.array_equal(pool2, pool) and np.array_equal(table2, table) and list(ctx2) == ctx
+    bad = free.copy()
+    bad[len(free) - 1] = pool.shape[0]  # out of the pool
+    pool3, table3, _, cnt3, err = kv_append(pool, table, ctx, k_new, v_new, bad, len(free), dtype)
+    assert err == {"bad_page"} and cnt3 == len(free) and np.array_equal(table3, table)
+    # a context that would overflow the page table row: that sequence is skipped
+    ctx_bad = [3, 14, 16 * table.shape[1] - 2]
+    _, table4, ctx4, _, err = kv_append(pool, table, ctx_bad, k_new, v_new, free, len(free), dtype)
+    assert err == {"bad_ctx"} and ctx4[2] == ctx_bad[2] and np.array_equal(table4[2], table[2])
+
+
+def test_rollback_clamps_and_reports():
+    table = np.array([[0, 1, -1], [2, -1, -1]], dtype=np.int32)
+    free = np.array([3, 4, 0, 0, 0], dtype=np.int32)
+    t2, c2, f2, n2, err = kv_rollback(table, [20, 9], [0, 9], 7, free, 2)
+    assert err == {"bad_len"}
+    assert list(c2) == [14, 9]  # accept_len clamped to 1 and 7
+    assert n2 == 3 and list(f2[:3]) == [3, 4, 1] and t2[0, 1] == -1
