@@ -164,6 +164,37 @@ def time_kv(ds, w, K):
             "kv_rollback": {"us": rb}}
 
 
+def time_propose(ds, w, K):
+    """Per-call time of idlm_isd_propose on the workload: this step's drafts
+    and accept lengths, the MASK rows standing in for the next forward's
+    (same shape), an attention call before each timed call."""
+    import torch
+
+    from speculative_verify_isd_amd import lib as L
+
+    if w.N == 1:
+        return {}
+    nxt = torch.empty_like(ds.drafts)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for k in range(K + 3):
+        ds.attn()
+        e = ev[k - 3] if k >= 3 else None
+        if e:
+            e[0].record()
+        L.idlm_isd_propose(ds.dims, ds.lm, ds.drafts, ds.lens, 7 + k, w.T, nxt, ds.ws)
+        if e:
+            e[1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([x[0].elapsed_time(x[1]) for x in ev])) * 1e3
+    lens = ds.lens.cpu().numpy()
+    kd = (w.draft_tokens >= 0).sum(axis=1)
+    cont = int((lens == kd + 1).sum())
+    es = 2 if w.logits_dtype == "bf16" else 4
+    nbytes = cont * (w.N - 1) * w.V * es  # rows of continuing sequences, read once
+    return {"propose": {"us": us, "continuing_sequences": cont, "algorithmic_bytes": nbytes,
+                        "GB/s": nbytes / (us * 1e-6) / 1e9}}
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -280,6 +311,7 @@ def main():
         graph_ms = g0.elapsed_time(g1) / K
 
     kv = time_kv(ds, w, K)
+    kv.update(time_propose(ds, w, K))
 
     lens = ds.lens.cpu().numpy()
     kp = (w.draft_tokens >= 0).sum(axis=1) if w.N > 1 else np.zeros(w.B, dtype=np.int64)

@@ -19,7 +19,9 @@
  *      truncated there ("Introspective Diffusion Language Models", section
  *      "Inference & ISD"; GeekNews summary, section "Inference & ISD").
  *   3. idlm_isd_step: 1 then 2 on one stream.
- *   4. idlm_isd_kv_append / idlm_isd_kv_rollback: the cache writes around a
+ *   4. idlm_isd_propose: the next step's drafts from this forward's MASK
+ *      rows, or a fresh step after a rejection.
+ *   5. idlm_isd_kv_append / idlm_isd_kv_rollback: the cache writes around a
  *      step (new rows in before attention, back to the accepted prefix
  *      after acceptance).
  *
@@ -168,6 +170,25 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
                       const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
                       int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
                       void* workspace, size_t ws_bytes, void* stream);
+
+/* Drafts for the next step.  MASK rows propose the next tokens from q
+ * ("Introspective Diffusion Language Models", section "Inference & ISD").
+ * A sequence whose listed drafts were all kept (accept_len == k + 1, k the
+ * drafts before the first -1; k = 0 is a fresh step) keeps verifying: draft
+ * i of its next step is drawn from softmax(logits_next[b][i] / T) by inverse
+ * CDF (ascending vocabulary, smallest v whose running sum exceeds u * sum)
+ * with u = word 0 of the Philox4x64-10 block at counter (i, 1, 0, 0) under
+ * key (seed, b), or the argmax (lowest index) when T == 0.  Otherwise the
+ * next step is fresh and all its drafts are -1.  No-op when N == 1.
+ *   logits_next  [device] [B][K][V] logits_dtype: this forward's MASK rows
+ *   draft_tokens [device] int32 [B][K]: this step's list
+ *   accept_len   [device] int32 [B]: idlm_isd_accept's output
+ *   next_drafts  [device] int32 [B][K], written
+ * Rows of sequences that start a fresh step are not read. */
+int32_t idlm_isd_propose(const idlm_isd_dims* d, const void* logits_next,
+                         const int32_t* draft_tokens, const int32_t* accept_len, uint64_t seed,
+                         float T, int32_t* next_drafts, void* workspace, size_t ws_bytes,
+                         void* stream);
 
 /* KV append, before attention.  Writes the R step rows' keys and values into
  * the paged cache at positions ctx_before[b] .. ctx_before[b]+R-1 (the cache

@@ -64,3 +64,11 @@ def isd_uniforms(seed, b, i):
     """(u_i, u'_i) for sequence ``b`` and draft position ``i`` under ``seed``."""
     w = philox4x64_10((i, 0, 0, 0), (seed, b))
     return word_to_uniform(w[0]), word_to_uniform(w[1])
+
+
+def propose_uniform(seed, b, i):
+    """Uniform for proposing draft ``i`` of sequence ``b``'s next step: word 0
+    of the block at counter (i, 1, 0, 0) under key (seed, b), a stream apart
+    from the acceptance uniforms (counter word 1 is 0 there)."""
+    w = philox4x64_10((i, 1, 0, 0), (seed, b))
+    return word_to_uniform(w[0])

@@ -796,6 +796,262 @@ int32_t launch_all(AccArgs a, int U1, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Proposals for the next step.
+//
+// MASK rows propose the next tokens from q ("Introspective Diffusion
+// Language Models", section "Inference & ISD").  A sequence whose listed
+// drafts were all kept (accept_len == k + 1) continues verifying: draft i of
+// its next step is drawn from softmax(next_i / T) by inverse CDF with the
+// uniform of Philox counter (i, 1, 0, 0); T = 0 takes the argmax.  Otherwise
+// the next step is fresh and its drafts are all -1.
+//
+//   propose_stats   grid B*K*ceil(nsub/8): each wave reduces whole 2048-element
+//                   sub-chunks to (max m_c, sum of exp2((l - m_c) c)) (greedy:
+//                   max, lowest argmax).  Rows of sequences that will not
+//                   continue are skipped, so their logits are never read.
+//   propose_select  grid B*K, one wave per row: weights s_c * 2^((m_c - M) c)
+//                   in sub-chunk order, a wave scan locates the sub-chunk
+//                   holding t = u * total, which is rescanned with the same
+//                   exponentials (relative to m_c) as the stats pass.
+// ---------------------------------------------------------------------------
+struct PropArgs {
+  const void* ln;           // [B][K][V]
+  const int32_t* drafts;    // [B][K] this step's list
+  const int32_t* accept_len;
+  int32_t* next;            // [B][K]
+  double2* st;              // [B][K][nsub]
+  uint64_t seed;
+  float c2;                 // log2(e) / T
+  int greedy, B, K, V, nsub, f32;
+};
+
+constexpr int kPropSubPerWave = 2;
+
+// Whether sequence b's next step verifies (all listed drafts kept).
+__device__ inline bool continues(const PropArgs& a, int b) {
+  int k = a.K;
+  for (int i = 0; i < a.K; ++i)
+    if (a.drafts[(size_t)b * a.K + i] < 0) {
+      k = i;
+      break;
+    }
+  return a.accept_len[b] == k + 1;
+}
+
+__device__ inline const void* prop_row(const PropArgs& a, int b, int i) {
+  const size_t es = a.f32 ? 4 : 2;
+  return (const char*)a.ln + ((size_t)b * a.K + i) * a.V * es;
+}
+
+template <bool VEC, bool F32>
+__global__ __launch_bounds__(256) void propose_stats_kernel(PropArgs a) {
+  constexpr int kSubPerWg = 4 * kPropSubPerWave;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int S = (a.nsub + kSubPerWg - 1) / kSubPerWg;
+  const int64_t wg = blockIdx.x;
+  const int slice = (int)(wg % S);
+  const int i = (int)((wg / S) % a.K);
+  const int b = (int)(wg / ((int64_t)S * a.K));
+  if (!continues(a, b)) return;
+  const void* row = prop_row(a, b, i);
+  double2* out = a.st + ((size_t)b * a.K + i) * a.nsub;
+  const int sc0 = slice * kSubPerWg + wave * kPropSubPerWave;
+  // Both sub-chunks' loads first (clamped to a real sub-chunk), then math.
+  Logits8<VEC, F32> x[kPropSubPerWave][4];
+#pragma unroll
+  for (int k = 0; k < kPropSubPerWave; ++k) {
+    const int sc = min(sc0 + k, a.nsub - 1);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) x[k][g] = load8<VEC, F32>(row, sc * kSub + 512 * g + 8 * lane, a.V);
+  }
+#pragma unroll
+  for (int k = 0; k < kPropSubPerWave; ++k) {
+    const int sc = sc0 + k;
+    if (sc >= a.nsub) break;  // wave-uniform
+    if (a.greedy) {
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int v = sc * kSub + 512 * g + 8 * lane + e;
+          if (v < a.V) better(bv, bi, x[k][g][e], v);
+        }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float vo = __shfl_xor(bv, off);
+        const int io = __shfl_xor(bi, off);
+        better(bv, bi, vo, io);
+      }
+      if (lane == 0) out[sc] = make_double2((double)bv, (double)bi);
+    } else {
+      float m = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, x[k][g][e]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      double s = 0.0;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part += __builtin_amdgcn_exp2f((x[k][g][e] - m) * a.c2);
+          s += (double)part;
+        }
+      }
+      s = wave_total(s);
+      if (lane == 0) out[sc] = make_double2((double)m, s);
+    }
+  }
+}
+
+template <bool VEC, bool F32>
+__global__ __launch_bounds__(64) void propose_select_kernel(PropArgs a) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / a.K, i = blockIdx.x % a.K;
+  int32_t* dst = a.next + (size_t)b * a.K + i;
+  if (!continues(a, b)) {
+    if (lane == 0) *dst = -1;
+    return;
+  }
+  const double2* st = a.st + ((size_t)b * a.K + i) * a.nsub;
+  const int per = (a.nsub + 63) / 64;
+  const int k0 = min(a.nsub, lane * per), k1 = min(a.nsub, k0 + per);
+  if (a.greedy) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int k = k0; k < k1; ++k) better(bv, bi, (float)st[k].x, (int)st[k].y);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float vo = __shfl_xor(bv, off);
+      const int io = __shfl_xor(bi, off);
+      better(bv, bi, vo, io);
+    }
+    if (lane == 0) *dst = bi == 0x7FFFFFFF ? 0 : bi;
+    return;
+  }
+  const double c2 = (double)a.c2;
+  double M = -INFINITY;
+  for (int k = k0; k < k1; ++k) M = fmax(M, st[k].x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmax(M, __shfl_xor(M, off));
+  // Sub-chunk weights in order; this lane's run sum, then a wave scan.
+  double ls = 0.0;
+  for (int k = k0; k < k1; ++k) {
+    const double2 v = st[k];
+    ls += v.x == -INFINITY ? 0.0 : v.y * exp2((v.x - M) * c2);
+  }
+  double inc = ls;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  const double W = __shfl(inc, 63);
+  double ex = __shfl_up(inc, 1);
+  if (lane == 0) ex = 0.0;
+  const double u = top24(philox4x64_10((uint64_t)i, 1, 0, 0, a.seed, (uint64_t)b).w[0]);
+  const double t = u * W;
+  // First sub-chunk with positive weight whose end exceeds t.
+  double run = ex, hbase = 0.0, hscale = 0.0;
+  int hit = -1, lastpos = -1;
+  for (int k = k0; k < k1; ++k) {
+    const double2 v = st[k];
+    const double f = v.x == -INFINITY ? 0.0 : exp2((v.x - M) * c2);
+    const double w = v.y * f;
+    if (w > 0.0) lastpos = k;
+    if (hit < 0 && w > 0.0 && run + w > t) {
+      hit = k;
+      hbase = run;
+      hscale = f;
+    }
+    run += w;
+  }
+  const unsigned long long hm = __ballot(hit >= 0);
+  int sc;
+  double tl;  // t relative to the sub-chunk, in its own units (weights relative to m_c)
+  bool past = false;
+  if (hm) {
+    const int src = (int)__builtin_ctzll(hm);
+    sc = __shfl(hit, src);
+    const double base = __shfl(hbase, src), scale = __shfl(hscale, src);
+    tl = fmax(0.0, (t - base) / scale);
+  } else {
+    const unsigned long long pm = __ballot(lastpos >= 0);
+    sc = pm ? __shfl(lastpos, 63 - (int)__builtin_clzll(pm)) : 0;
+    tl = 0.0;
+    past = true;
+  }
+  const float mc = (float)st[sc].x;
+  // Rescan: lane l owns elements sc*kSub + 32 l .. + 31 (vocabulary order).
+  const void* row = prop_row(a, b, i);
+  const int v0 = sc * kSub + kSelPer * lane;
+  Logits8<VEC, F32> xs[kSelPer / 8];
+#pragma unroll
+  for (int g = 0; g < kSelPer / 8; ++g) xs[g] = load8<VEC, F32>(row, v0 + 8 * g, a.V);
+  float w[kSelPer];
+  double ll = 0.0;
+  int lastp = -1;
+#pragma unroll
+  for (int g = 0; g < kSelPer / 8; ++g) {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = xs[g][e];
+      w[8 * g + e] = x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((x - mc) * a.c2);
+      part += w[8 * g + e];
+      if (w[8 * g + e] > 0.f) lastp = v0 + 8 * g + e;
+    }
+    ll += (double)part;
+  }
+  double li = ll;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(li, off);
+    if (lane >= off) li += y;
+  }
+  double le = __shfl_up(li, 1);
+  if (lane == 0) le = 0.0;
+  const bool holder = !past && le <= tl && tl < li;
+  int tok = lastp;
+  if (holder) {
+    double r = le;
+    bool done = false;
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+      r += (double)w[e];
+      if (!done && r > tl) {
+        tok = v0 + e;
+        done = true;
+      }
+    }
+  }
+  const unsigned long long hm2 = __ballot(holder);
+  const unsigned long long pm2 = __ballot(lastp >= 0);
+  if (hm2)
+    tok = __shfl(tok, (int)__builtin_ctzll(hm2));
+  else
+    tok = pm2 ? __shfl(lastp, 63 - (int)__builtin_clzll(pm2)) : min(a.V - 1, sc * kSub);
+  if (lane == 0) *dst = tok;
+}
+
+template <bool VEC, bool F32>
+int32_t launch_propose_t(PropArgs a, hipStream_t s) {
+  constexpr int kSubPerWg = 4 * kPropSubPerWave;
+  const int S = (a.nsub + kSubPerWg - 1) / kSubPerWg;
+  const int64_t g1 = (int64_t)a.B * a.K * S;
+  hipLaunchKernelGGL((propose_stats_kernel<VEC, F32>), dim3((unsigned)g1), dim3(256), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
+  hipLaunchKernelGGL((propose_select_kernel<VEC, F32>), dim3((unsigned)(a.B * a.K)), dim3(64), 0,
+                     s, a);
+  return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
+}
+
 }  // namespace
 
 int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
@@ -834,6 +1090,33 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
                    (lm == nullptr || ((uintptr_t)lm % 16) == 0);
   if (a.f32) return vec ? launch_all<true, true>(a, ap.U1, s) : launch_all<false, true>(a, ap.U1, s);
   return vec ? launch_all<true, false>(a, ap.U1, s) : launch_all<false, false>(a, ap.U1, s);
+}
+
+}  // namespace idlm
+
+namespace idlm {
+
+int32_t launch_propose(const idlm_isd_dims& d, const Plan& p, const void* logits_next,
+                       const int32_t* drafts, const int32_t* accept_len, uint64_t seed, float T,
+                       int32_t* next_drafts, char* ws, hipStream_t s) {
+  if (d.B == 0 || d.N == 1) return IDLM_OK;
+  PropArgs a = {};
+  a.ln = logits_next;
+  a.drafts = drafts;
+  a.accept_len = accept_len;
+  a.next = next_drafts;
+  a.st = (double2*)(ws + p.off_pstats);
+  a.seed = seed;
+  a.greedy = (T == 0.0f);
+  a.c2 = a.greedy ? 0.f : (float)(1.4426950408889634 / (double)T);
+  a.B = d.B;
+  a.K = d.N - 1;
+  a.V = d.V;
+  a.nsub = p.acc.nsub;
+  a.f32 = d.logits_dtype == IDLM_F32;
+  const bool vec = d.V % 8 == 0 && ((uintptr_t)logits_next % 16) == 0;
+  if (a.f32) return vec ? launch_propose_t<true, true>(a, s) : launch_propose_t<false, true>(a, s);
+  return vec ? launch_propose_t<true, false>(a, s) : launch_propose_t<false, false>(a, s);
 }
 
 }  // namespace idlm

@@ -86,6 +86,9 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   o = align256(o + (size_t)d.B * 16 * 16);
   p->off_kv_valid = o;
   o = align256(o + (size_t)d.B);
+  // Proposal statistics: (max, sum) per sub-chunk of every next-step MASK row.
+  p->off_pstats = o;
+  o = align256(o + (size_t)d.B * (d.N - 1) * c.nsub * 16);
   p->total = o;
   return true;
 }
@@ -190,6 +193,22 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
   if (r != IDLM_OK) return r;
   return launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
                        out_accept_len, nullptr, (char*)workspace, s);
+}
+
+int32_t idlm_isd_propose(const idlm_isd_dims* d, const void* logits_next,
+                         const int32_t* draft_tokens, const int32_t* accept_len, uint64_t seed,
+                         float T, int32_t* next_drafts, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  int32_t r = check_dims(d);
+  if (r != IDLM_OK) return r;
+  if ((r = check_T(T)) != IDLM_OK) return r;
+  Plan p;
+  make_plan(*d, &p);
+  if ((r = check_ws(p, workspace, ws_bytes)) != IDLM_OK) return r;
+  if (d->B == 0 || d->N == 1) return IDLM_OK;
+  if (!logits_next || !draft_tokens || !accept_len || !next_drafts) return IDLM_ERR_NULL;
+  return launch_propose(*d, p, logits_next, draft_tokens, accept_len, seed, T, next_drafts,
+                        (char*)workspace, (hipStream_t)stream);
 }
 
 int32_t idlm_isd_kv_append(const idlm_isd_dims* d, const void* k_new, const void* v_new,

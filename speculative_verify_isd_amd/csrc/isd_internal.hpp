@@ -58,7 +58,7 @@ struct Plan {
   AcceptPlan acc;
   size_t off_status, off_attn_ml, off_attn_o;
   size_t off_splan, off_stats, off_subsum, off_dlog, off_unif;
-  size_t off_kv_valid;
+  size_t off_kv_valid, off_pstats;
   size_t total;
 };
 
@@ -73,6 +73,10 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
                       int32_t* out_len, double* out_debug, char* ws, hipStream_t s);
 
 int32_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
+
+int32_t launch_propose(const idlm_isd_dims& d, const Plan& p, const void* logits_next,
+                       const int32_t* drafts, const int32_t* accept_len, uint64_t seed, float T,
+                       int32_t* next_drafts, char* ws, hipStream_t s);
 
 int32_t launch_kv_append(const idlm_isd_dims& d, const Plan& p, const void* k_new,
                          const void* v_new, const int32_t* ctx_before, int32_t* ctx_after,

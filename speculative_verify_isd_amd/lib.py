@@ -37,6 +37,7 @@ ENTRY_POINTS = (
     "idlm_isd_paged_attn",
     "idlm_isd_accept",
     "idlm_isd_step",
+    "idlm_isd_propose",
     "idlm_isd_kv_append",
     "idlm_isd_kv_rollback",
     "idlm_isd_read_status",
@@ -87,6 +88,7 @@ def load():
         "idlm_isd_paged_attn": (i32, [D, P, P, P, P, P, P, sz, P]),
         "idlm_isd_accept": (i32, [D, P, P, P, u64, f32, P, P, P, P, sz, P]),
         "idlm_isd_step": (i32, [D, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, sz, P]),
+        "idlm_isd_propose": (i32, [D, P, P, P, u64, f32, P, P, sz, P]),
         "idlm_isd_kv_append": (i32, [D, P, P, P, P, P, P, P, P, P, sz, P]),
         "idlm_isd_kv_rollback": (i32, [D, P, P, P, P, P, P, P, sz, P]),
         "idlm_isd_read_status": (i32, [P, P, ctypes.POINTER(i32)]),
@@ -211,6 +213,16 @@ def idlm_isd_step(dims, q, kv_pages, page_table, ctx_lens, logits_clean, logits_
         _ptr(out_tokens, _i32(), "out_tokens"), _ptr(out_accept_len, _i32(), "out_accept_len"),
         _ptr(attn_out, fq, "attn_out"), _ptr(ws, (torch.uint8,), "workspace"), ws.numel(),
         _stream()), "idlm_isd_step")
+
+
+def idlm_isd_propose(dims, logits_next, draft_tokens, accept_len, seed, T, next_drafts, ws):
+    _check(load().idlm_isd_propose(
+        ctypes.byref(dims), _ptr(logits_next, _fdt(dims.logits_dtype), "logits_next"),
+        _ptr(draft_tokens, _i32(), "draft_tokens"), _ptr(accept_len, _i32(), "accept_len"),
+        ctypes.c_uint64(int(seed) & (2**64 - 1)), ctypes.c_float(float(T)),
+        _ptr(next_drafts, _i32(), "next_drafts"), _ptr(ws, (_torch().uint8,), "workspace"),
+        ctypes.c_size_t(ws.numel()), _stream()),
+        "idlm_isd_propose")
 
 
 def idlm_isd_kv_append(dims, k_new, v_new, ctx_before, ctx_after, kv_pages, page_table,
