@@ -195,6 +195,42 @@ def time_propose(ds, w, K):
                         "GB/s": nbytes / (us * 1e-6) / 1e9}}
 
 
+def time_lora(ds, w, K, H=4096, O=4096, rank=128):
+    """Per-call time of idlm_isd_gated_lora for the workload's rows (B blocks
+    of 2N-1) on one projection of a Qwen3-8B-sized layer (H = O = 4096) with a
+    rank-128 adapter; synthetic device inputs."""
+    import torch
+
+    from speculative_verify_isd_amd import lib as L
+
+    R = 2 * w.N - 1
+    M, Mq = w.B * R, w.B * (w.N - 1)
+    ld = L.LoraDims(w.B, w.N, H, O, rank)
+    ws = L.alloc_lora_workspace(ld)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    y = torch.randn((M, O), device="cuda", generator=g)
+    x = torch.randn((M, H), device="cuda", generator=g).to(torch.bfloat16)
+    a = (torch.randn((rank, H), device="cuda", generator=g) / 64).to(torch.bfloat16)
+    b = (torch.randn((O, rank), device="cuda", generator=g) / 20).to(torch.bfloat16)
+    out = torch.empty((M, O), dtype=torch.bfloat16, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for k in range(K + 3):
+        ds.attn()
+        e = ev[k - 3] if k >= 3 else None
+        if e:
+            e[0].record()
+        L.idlm_isd_gated_lora(ld, y, x, a, b, 2.0, out, ws)
+        if e:
+            e[1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([x_[0].elapsed_time(x_[1]) for x_ in ev])) * 1e3
+    nbytes = M * O * 4 + M * O * 2 + Mq * H * 2 + rank * H * 2 + O * rank * 2
+    flops = 2 * Mq * H * rank + 2 * Mq * O * rank
+    return {"gated_lora": {"us": us, "shape": f"M={M} (MASK rows {Mq}), H={H}, O={O}, rank={rank}",
+                           "algorithmic_bytes": nbytes, "GB/s": nbytes / (us * 1e-6) / 1e9,
+                           "TFLOP/s": flops / (us * 1e-6) / 1e12}}
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -312,6 +348,7 @@ def main():
 
     kv = time_kv(ds, w, K)
     kv.update(time_propose(ds, w, K))
+    kv.update(time_lora(ds, w, K))
 
     lens = ds.lens.cpu().numpy()
     kp = (w.draft_tokens >= 0).sum(axis=1) if w.N > 1 else np.zeros(w.B, dtype=np.int64)

@@ -21,7 +21,9 @@
  *   3. idlm_isd_step: 1 then 2 on one stream.
  *   4. idlm_isd_propose: the next step's drafts from this forward's MASK
  *      rows, or a fresh step after a rejection.
- *   5. idlm_isd_kv_append / idlm_isd_kv_rollback: the cache writes around a
+ *   5. idlm_isd_gated_lora: R-ISD's adapter on MASK rows after the base
+ *      projection (verify rows untouched).
+ *   6. idlm_isd_kv_append / idlm_isd_kv_rollback: the cache writes around a
  *      step (new rows in before attention, back to the accepted prefix
  *      after acceptance).
  *
@@ -189,6 +191,42 @@ int32_t idlm_isd_propose(const idlm_isd_dims* d, const void* logits_next,
                          const int32_t* draft_tokens, const int32_t* accept_len, uint64_t seed,
                          float T, int32_t* next_drafts, void* workspace, size_t ws_bytes,
                          void* stream);
+
+/* Sizes of a gated-LoRA call.  Passed by [host] pointer. */
+typedef struct {
+  int32_t B, N;   /* rows: B blocks of R = 2N-1; row r of a block is a MASK row iff r >= N */
+  int32_t H;      /* input features, multiple of 32                        */
+  int32_t O;      /* output features, >= 1                                 */
+  int32_t rank;   /* adapter rank, multiple of 16, <= 256                  */
+} idlm_isd_lora_dims;
+
+/* Workspace bytes idlm_isd_gated_lora needs (0 for invalid sizes).  Host only. */
+size_t idlm_isd_lora_workspace_bytes(const idlm_isd_lora_dims* L);
+
+/* R-ISD's gated LoRA, applied after the base projection: the adapter is
+ * active only at MASK rows and verify rows keep the base weights alone, which
+ * makes the output bit-for-bit the base model's ("Introspective Diffusion
+ * Language Models", section "Lossless R-ISD").
+ *   y_base [device] float32 [M][O], M = B*(2N-1): the base projection's
+ *          accumulator, before rounding
+ *   x      [device] bf16 [M][H] (16-byte aligned): the projection's input rows
+ *   lora_a [device] bf16 [rank][H], lora_b [device] bf16 [O][rank] (aligned)
+ *   y_out  [device] bf16 [M][O], written
+ * Verify rows: y_out = bf16(y_base), nothing else (bit-identical to the
+ * base-only output).  MASK rows: y_out = bf16(y_base + scale * (x A^T) B^T),
+ * the adapter products accumulated in float32, rounded once to nearest even.
+ * Workspace: idlm_isd_lora_workspace_bytes, 256-byte aligned, no init
+ * needed (split partials of x A^T and their sum).  All buffers are the
+ * caller's; y_out must not overlap y_base, x or the workspace.  Kernels are
+ * enqueued on `stream`; nothing is synchronised.
+ * Errors (nothing enqueued): IDLM_ERR_NULL for a null pointer,
+ * IDLM_ERR_DIMS for sizes out of range or a non-finite scale,
+ * IDLM_ERR_UNSUPPORTED for H not a multiple of 32, rank not a multiple of
+ * 16 or above 256, or x / lora_a / lora_b not 16-byte aligned,
+ * IDLM_ERR_WORKSPACE for a short or misaligned workspace.  B = 0 is a no-op. */
+int32_t idlm_isd_gated_lora(const idlm_isd_lora_dims* L, const float* y_base, const void* x,
+                            const void* lora_a, const void* lora_b, float scale, void* y_out,
+                            void* workspace, size_t ws_bytes, void* stream);
 
 /* KV append, before attention.  Writes the R step rows' keys and values into
  * the paged cache at positions ctx_before[b] .. ctx_before[b]+R-1 (the cache

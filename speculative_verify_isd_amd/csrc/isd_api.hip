@@ -211,6 +211,38 @@ int32_t idlm_isd_propose(const idlm_isd_dims* d, const void* logits_next,
                         (char*)workspace, (hipStream_t)stream);
 }
 
+static int32_t check_lora(const idlm_isd_lora_dims* L) {
+  if (!L) return IDLM_ERR_NULL;
+  if (L->B < 0 || L->B > (1 << 20) || L->N < 1 || L->N > 16) return IDLM_ERR_DIMS;
+  if (L->H < 1 || L->O < 1 || L->rank < 1) return IDLM_ERR_DIMS;
+  if ((int64_t)L->B * (2 * L->N - 1) * L->O > (1ll << 31)) return IDLM_ERR_DIMS;
+  if (L->H % 32 != 0 || L->H > (1 << 20) || L->rank % 16 != 0 || L->rank > 256)
+    return IDLM_ERR_UNSUPPORTED;
+  return IDLM_OK;
+}
+
+size_t idlm_isd_lora_workspace_bytes(const idlm_isd_lora_dims* L) {
+  if (check_lora(L) != IDLM_OK) return 0;
+  const size_t n = gated_lora_workspace(*L);
+  return align256(n > 0 ? n : 256);
+}
+
+int32_t idlm_isd_gated_lora(const idlm_isd_lora_dims* L, const float* y_base, const void* x,
+                            const void* lora_a, const void* lora_b, float scale, void* y_out,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  int32_t r = check_lora(L);
+  if (r != IDLM_OK) return r;
+  if (!isfinite(scale)) return IDLM_ERR_DIMS;
+  const size_t need = idlm_isd_lora_workspace_bytes(L);
+  if (!workspace) return IDLM_ERR_NULL;
+  if (((uintptr_t)workspace & 255) != 0 || ws_bytes < need) return IDLM_ERR_WORKSPACE;
+  if (L->B == 0) return IDLM_OK;
+  if (!y_base || !x || !lora_a || !lora_b || !y_out) return IDLM_ERR_NULL;
+  if (((uintptr_t)x | (uintptr_t)lora_a | (uintptr_t)lora_b) & 15) return IDLM_ERR_UNSUPPORTED;
+  return launch_gated_lora(*L, y_base, x, lora_a, lora_b, scale, y_out, (char*)workspace,
+                           (hipStream_t)stream);
+}
+
 int32_t idlm_isd_kv_append(const idlm_isd_dims* d, const void* k_new, const void* v_new,
                            const int32_t* ctx_before, int32_t* ctx_after, void* kv_pages,
                            int32_t* page_table, int32_t* free_pages, int32_t* free_count,

@@ -74,6 +74,12 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
 
 int32_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
 
+// Gated LoRA: workspace bytes (split partials and T) and the launcher.
+size_t gated_lora_workspace(const idlm_isd_lora_dims& L);
+int32_t launch_gated_lora(const idlm_isd_lora_dims& L, const float* y_base, const void* x,
+                          const void* lora_a, const void* lora_b, float scale, void* y_out,
+                          char* ws, hipStream_t s);
+
 int32_t launch_propose(const idlm_isd_dims& d, const Plan& p, const void* logits_next,
                        const int32_t* drafts, const int32_t* accept_len, uint64_t seed, float T,
                        int32_t* next_drafts, char* ws, hipStream_t s);

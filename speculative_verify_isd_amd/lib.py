@@ -38,6 +38,8 @@ ENTRY_POINTS = (
     "idlm_isd_accept",
     "idlm_isd_step",
     "idlm_isd_propose",
+    "idlm_isd_lora_workspace_bytes",
+    "idlm_isd_gated_lora",
     "idlm_isd_kv_append",
     "idlm_isd_kv_rollback",
     "idlm_isd_read_status",
@@ -57,6 +59,11 @@ class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "B", "N", "Hq", "Hkv", "D", "V", "page_size", "max_pages", "num_pages",
         "qkv_dtype", "logits_dtype")]
+
+
+class LoraDims(ctypes.Structure):
+    """idlm_isd_lora_dims."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "N", "H", "O", "rank")]
 
 
 def make_dims(B, N, Hq, Hkv, D, V, max_pages, num_pages, qkv_dtype="bf16", logits_dtype="bf16",
@@ -89,6 +96,8 @@ def load():
         "idlm_isd_accept": (i32, [D, P, P, P, u64, f32, P, P, P, P, sz, P]),
         "idlm_isd_step": (i32, [D, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, sz, P]),
         "idlm_isd_propose": (i32, [D, P, P, P, u64, f32, P, P, sz, P]),
+        "idlm_isd_lora_workspace_bytes": (sz, [ctypes.POINTER(LoraDims)]),
+        "idlm_isd_gated_lora": (i32, [ctypes.POINTER(LoraDims), P, P, P, P, f32, P, P, sz, P]),
         "idlm_isd_kv_append": (i32, [D, P, P, P, P, P, P, P, P, P, sz, P]),
         "idlm_isd_kv_rollback": (i32, [D, P, P, P, P, P, P, P, sz, P]),
         "idlm_isd_read_status": (i32, [P, P, ctypes.POINTER(i32)]),
@@ -223,6 +232,31 @@ def idlm_isd_propose(dims, logits_next, draft_tokens, accept_len, seed, T, next_
         _ptr(next_drafts, _i32(), "next_drafts"), _ptr(ws, (_torch().uint8,), "workspace"),
         ctypes.c_size_t(ws.numel()), _stream()),
         "idlm_isd_propose")
+
+
+def idlm_isd_lora_workspace_bytes(ldims):
+    return int(load().idlm_isd_lora_workspace_bytes(ctypes.byref(ldims)))
+
+
+def alloc_lora_workspace(ldims, device="cuda"):
+    torch = _torch()
+    n = idlm_isd_lora_workspace_bytes(ldims)
+    if n == 0:
+        raise IdlmError(2, "idlm_isd_lora_workspace_bytes")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def idlm_isd_gated_lora(ldims, y_base, x, lora_a, lora_b, scale, y_out, ws):
+    torch = _torch()
+    bf = (torch.bfloat16,)
+    _check(load().idlm_isd_gated_lora(
+        ctypes.byref(ldims), _ptr(y_base, (torch.float32,), "y_base"), _ptr(x, bf, "x"),
+        _ptr(lora_a, bf, "lora_a"), _ptr(lora_b, bf, "lora_b"), ctypes.c_float(float(scale)),
+        _ptr(y_out, bf, "y_out"), _ptr(ws, (torch.uint8,), "workspace"),
+        ctypes.c_size_t(ws.numel()), _stream()),
+        "idlm_isd_gated_lora")
 
 
 def idlm_isd_kv_append(dims, k_new, v_new, ctx_before, ctx_after, kv_pages, page_table,

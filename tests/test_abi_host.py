@@ -139,3 +139,23 @@ def test_kv_append_rejects_before_launch(so):
     ne = L.idlm_isd_workspace_bytes(e)
     assert so.idlm_isd_kv_append(ctypes.byref(e), *([None] * 8), fake, ne, None) == 0
     assert so.idlm_isd_kv_rollback(ctypes.byref(e), *([None] * 6), fake, ne, None) == 0
+
+
+def test_gated_lora_validates_before_launch(so):
+    ok = L.LoraDims(64, 4, 4096, 4096, 128)
+    n = L.idlm_isd_lora_workspace_bytes(ok)
+    assert n > 0 and n % 256 == 0
+    for bad, code in ((L.LoraDims(64, 4, 4004, 4096, 128), 3), (L.LoraDims(64, 4, 4096, 4096, 100), 3),
+                      (L.LoraDims(64, 0, 4096, 4096, 128), 2), (L.LoraDims(-1, 4, 4096, 64, 16), 2)):
+        assert L.idlm_isd_lora_workspace_bytes(bad) == 0
+        assert so.idlm_isd_gated_lora(ctypes.byref(bad), None, None, None, None, ctypes.c_float(1.0),
+                                      None, None, 0, None) == code
+    fake = ctypes.c_void_p(1 << 20)
+    assert so.idlm_isd_gated_lora(ctypes.byref(ok), fake, fake, fake, fake, ctypes.c_float(1.0),
+                                  fake, fake, n - 256, None) == 5
+    assert so.idlm_isd_gated_lora(ctypes.byref(ok), None, fake, fake, fake, ctypes.c_float(1.0),
+                                  fake, fake, n, None) == 1
+    assert so.idlm_isd_gated_lora(ctypes.byref(ok), fake, ctypes.c_void_p((1 << 20) + 2), fake,
+                                  fake, ctypes.c_float(1.0), fake, fake, n, None) == 3
+    assert so.idlm_isd_gated_lora(ctypes.byref(ok), fake, fake, fake, fake,
+                                  ctypes.c_float(float("nan")), fake, fake, n, None) == 2
