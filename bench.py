@@ -47,13 +47,15 @@ def attn_bytes(w):
 
 
 def accept_bytes(w, lens, kp):
-    """Algorithmic HBM bytes of one acceptance launch pair: all 2N-1 logit rows
-    once, then the residual pair (p_j and q_j rows) or the bonus row once."""
+    """Algorithmic HBM bytes of one acceptance call: all 2N-1 logit rows once;
+    after a rejection the residual pair (p_j and q_j rows) once more; with
+    every draft kept, one 2048-entry sub-chunk of the bonus row (its
+    sub-chunk sums come from the first pass)."""
     es = 2 if w.logits_dtype == "bf16" else 4
     rows = w.B * w.R
     resid = int(((lens - 1) < kp).sum())
     bonus = w.B - resid
-    return (rows + 2 * resid + bonus) * w.V * es + w.B * (w.N + 1) * 4
+    return ((rows + 2 * resid) * w.V + bonus * min(2048, w.V)) * es + w.B * (w.N + 1) * 4
 
 
 def measured_traffic():

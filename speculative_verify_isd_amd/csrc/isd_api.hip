@@ -54,10 +54,11 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   AcceptPlan& c = p->acc;
   c.R = 2 * d.N - 1;
   c.nsub = (int)ceil_div(d.V, kSub);
-  // Stats: the widest per-thread batch that still gives >= 2048 work-groups.
+  // Stats: the widest per-thread batch (at most 4 vectors: measured faster
+  // than 8 at C = 64) that still gives >= 2048 work-groups.
   const int64_t rows = (int64_t)std::max(d.B, 1) * c.R;
   c.U1 = 1;
-  for (int u = 8; u >= 1; u /= 2)
+  for (int u = 4; u >= 1; u /= 2)
     if (rows * ceil_div(d.V, (int64_t)kSub * u) >= 2048) {
       c.U1 = u;
       break;
@@ -89,6 +90,9 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   // Proposal statistics: (max, sum) per sub-chunk of every next-step MASK row.
   p->off_pstats = o;
   o = align256(o + (size_t)d.B * (d.N - 1) * c.nsub * 16);
+  // Acceptance: (max, sum) per sub-chunk of each sequence's bonus row.
+  p->off_bstats = o;
+  o = align256(o + (size_t)d.B * c.nsub * 16);
   p->total = o;
   return true;
 }

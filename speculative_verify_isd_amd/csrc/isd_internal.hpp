@@ -58,7 +58,7 @@ struct Plan {
   AcceptPlan acc;
   size_t off_status, off_attn_ml, off_attn_o;
   size_t off_splan, off_stats, off_subsum, off_dlog, off_unif;
-  size_t off_kv_valid, off_pstats;
+  size_t off_kv_valid, off_pstats, off_bstats;
   size_t total;
 };
 
