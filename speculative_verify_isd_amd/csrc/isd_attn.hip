@@ -463,11 +463,11 @@ template <int D, int WR>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * WR;
   constexpr int kMergeVec = (ROWS * D / 4 + 255) / 256;  // float4 outputs per thread
-  constexpr int kMergeBlock = 16;                         // pieces per LDS block
-  constexpr int kBatch = kMergeVec < 16 ? 16 / kMergeVec : 1;  // pieces loaded together
+  constexpr int kBatch = kMergeVec < 32 ? 32 / kMergeVec : 1;  // pieces loaded together
+  constexpr int kMlHeld = kBatch < 8 ? 8 : kBatch;  // pieces' (max, sum) a row thread holds
   __shared__ int64_t sh_sum[4][2];
   __shared__ float sh_M[ROWS], sh_iL[ROWS];
-  __shared__ float sh_f[kMergeBlock][ROWS];
+  __shared__ float sh_f[kBatch][ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pair = blockIdx.x;
   const int b = pair / a.Hkv, h = pair % a.Hkv;
@@ -504,63 +504,80 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   auto slot_of = [&](int k) -> size_t {
     return (size_t)(wa + k) * 2 + ((k == 0 && start != (int64_t)wa * span) ? 1 : 0);
   };
-  // Row maxima and normalisers over all pieces.
+  // Each thread owns up to kMergeVec 4-wide d groups of the R*G x D output.
+  // The first kBatch pieces' partial outputs are loaded before anything
+  // waits, together with the pieces' (max, sum) rows, so a pair of up to
+  // kBatch pieces costs one round of loads after the lane range.
+  constexpr int D4 = D / 4;
+  const int nvec = a.RG * D4;
+  auto load_batch = [&](int k0, float4 (&v)[kBatch][kMergeVec]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int k = min(k0 + t, npieces - 1);  // clamped, unconditional
+      const float4* po = (const float4*)(a.part_o + slot_of(k) * ROWS * D);
+#pragma unroll
+      for (int e = 0; e < kMergeVec; ++e) v[t][e] = po[min(tid + 256 * e, nvec - 1)];
+    }
+  };
+  float4 v[kBatch][kMergeVec];
+  load_batch(0, v);
+  // Row maxima and normalisers over all pieces (row threads), the first
+  // kMlHeld pieces' (max, sum) kept in registers.
+  float2 mlr[kMlHeld];
   if (tid < a.RG) {
+#pragma unroll
+    for (int j = 0; j < kMlHeld; ++j) mlr[j] = a.part_ml[slot_of(min(j, npieces - 1)) * ROWS + tid];
     float M = -INFINITY;
-#pragma unroll 4
-    for (int k = 0; k < npieces; ++k) M = fmaxf(M, a.part_ml[slot_of(k) * ROWS + tid].x);
+#pragma unroll
+    for (int j = 0; j < kMlHeld; ++j)
+      if (j < npieces) M = fmaxf(M, mlr[j].x);
+    for (int k = kMlHeld; k < npieces; ++k) M = fmaxf(M, a.part_ml[slot_of(k) * ROWS + tid].x);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float L = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < npieces; ++k) {
+#pragma unroll
+    for (int j = 0; j < kMlHeld; ++j)
+      if (j < npieces) L += mlr[j].y * exp2f(mlr[j].x - Mu);
+    for (int k = kMlHeld; k < npieces; ++k) {
       const float2 ml = a.part_ml[slot_of(k) * ROWS + tid];
       L += ml.y * exp2f(ml.x - Mu);
     }
     sh_M[tid] = Mu;
     sh_iL[tid] = 1.f / L;
+    // Scale factors of the first batch.
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t)
+      sh_f[t][tid] = t < npieces ? exp2f(mlr[t].x - Mu) * (1.f / L) : 0.f;
   }
   __syncthreads();
-  // Each thread owns up to kMergeVec 4-wide d groups of the R*G x D output;
-  // pieces are folded in blocks whose scale factors sit in LDS, kBatch
-  // pieces' loads at a time (clamped to a real piece, with factor 0).
-  constexpr int D4 = D / 4;
-  const int nvec = a.RG * D4;
   float4 O[kMergeVec];
 #pragma unroll
   for (int e = 0; e < kMergeVec; ++e) O[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int kb = 0; kb < npieces; kb += kMergeBlock) {
-    const int nk = min(kMergeBlock, npieces - kb);
-    for (int i = tid; i < kMergeBlock * a.RG; i += 256) {
-      const int k = i / a.RG, row = i % a.RG;
-      sh_f[k][row] = k < nk ? exp2f(a.part_ml[slot_of(kb + k) * ROWS + row].x - sh_M[row]) * sh_iL[row]
-                            : 0.f;
-    }
-    __syncthreads();
-    for (int k0 = 0; k0 < nk; k0 += kBatch) {
-      float4 v[kBatch][kMergeVec];
+  // Fold the pieces in unit order, kBatch at a time.
+  for (int k0 = 0; k0 < npieces; k0 += kBatch) {
+    if (k0 > 0) {
+      __syncthreads();  // the previous batch's factors are consumed
+      load_batch(k0, v);
+      if (tid < a.RG) {
+        const float Mu = sh_M[tid], iL = sh_iL[tid];
 #pragma unroll
-      for (int t = 0; t < kBatch; ++t) {
-        const int k = min(k0 + t, nk - 1);
-        const float4* po = (const float4*)(a.part_o + slot_of(kb + k) * ROWS * D);
-#pragma unroll
-        for (int e = 0; e < kMergeVec; ++e) {
-          const int i = min(tid + 256 * e, nvec - 1);
-          v[t][e] = po[(i / D4) * D4 + i % D4];
-        }
+        for (int t = 0; t < kBatch; ++t)
+          sh_f[t][tid] = k0 + t < npieces
+                             ? exp2f(a.part_ml[slot_of(k0 + t) * ROWS + tid].x - Mu) * iL
+                             : 0.f;
       }
-#pragma unroll
-      for (int t = 0; t < kBatch; ++t)
-#pragma unroll
-        for (int e = 0; e < kMergeVec; ++e) {
-          const int i = min(tid + 256 * e, nvec - 1);
-          const float f = k0 + t < nk ? sh_f[k0 + t][i / D4] : 0.f;
-          O[e].x += v[t][e].x * f;
-          O[e].y += v[t][e].y * f;
-          O[e].z += v[t][e].z * f;
-          O[e].w += v[t][e].w * f;
-        }
+      __syncthreads();
     }
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t)
+#pragma unroll
+      for (int e = 0; e < kMergeVec; ++e) {
+        const int i = min(tid + 256 * e, nvec - 1);
+        const float f = sh_f[t][i / D4];
+        O[e].x += v[t][e].x * f;
+        O[e].y += v[t][e].y * f;
+        O[e].z += v[t][e].z * f;
+        O[e].w += v[t][e].w * f;
+      }
   }
   u16* outp = (u16*)a.out;
 #pragma unroll
