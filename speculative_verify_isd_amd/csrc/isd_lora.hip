@@ -166,9 +166,11 @@ __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(LoraArgs a) {
 
 // T = sum over shares ks = 0, 1, ... of the partials, one float4 per thread;
 // the loads of up to 16 shares are in flight together.
-__global__ __launch_bounds__(256) void lora_sum_kernel(LoraArgs a) {
+constexpr int kSumThreads = 64;  // small work-groups: the partials spread over many CUs
+
+__global__ __launch_bounds__(kSumThreads) void lora_sum_kernel(LoraArgs a) {
   const int64_t n4 = (int64_t)a.Mq * a.rank / 4;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * kSumThreads + threadIdx.x;
   if (i >= n4) return;
   const float4* p = (const float4*)a.tpart + i;
   float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -194,12 +196,10 @@ __global__ __launch_bounds__(256) void lora_sum_kernel(LoraArgs a) {
 inline size_t up_lds(int rank, int NB) {
   return (size_t)16 * (rank + 4) * 4 + (size_t)64 * NB * (rank + 4) * 2;
 }
-// Widest tile (4, 2 or 1 blocks per wave) whose LDS fits 64 KiB.
-inline int up_blocks(int rank) {
-  int nb = 4;
-  while (nb > 1 && up_lds(rank, nb) > 65536) nb /= 2;
-  return nb;
-}
+// One 16-column block per wave (64 columns per work-group): more, smaller
+// work-groups measured faster than 128-column tiles (7.4 vs 8.2 us at
+// M = 448, H = O = 4096, rank 128); LDS stays under 50 KiB up to rank 256.
+constexpr int kUpBlocks = 1;
 
 // Grid: ceil(Mq/16) row tiles x ceil(O / (64 NB)) column tiles.  T rows and
 // weight rows are staged in LDS, then each wave runs NB 16x16 float32 MFMA
@@ -344,18 +344,12 @@ int32_t launch_gated_lora(const idlm_isd_lora_dims& L, const float* y_base, cons
   hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)g1), dim3(kDownThreads), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
   if (a.Mq == 0) return IDLM_OK;
-  const unsigned gs = (unsigned)(((int64_t)a.Mq * a.rank / 4 + 255) / 256);
-  hipLaunchKernelGGL(lora_sum_kernel, dim3(gs), dim3(256), 0, s, a);
+  const unsigned gs = (unsigned)(((int64_t)a.Mq * a.rank / 4 + kSumThreads - 1) / kSumThreads);
+  hipLaunchKernelGGL(lora_sum_kernel, dim3(gs), dim3(kSumThreads), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
-  const int NB = up_blocks(a.rank);
+  constexpr int NB = kUpBlocks;
   const unsigned g2 = (unsigned)((a.Mq + 15) / 16 * ((a.O + 64 * NB - 1) / (64 * NB)));
-  const size_t lds = up_lds(a.rank, NB);
-  if (NB == 4)
-    hipLaunchKernelGGL((lora_up_kernel<4>), dim3(g2), dim3(256), lds, s, a);
-  else if (NB == 2)
-    hipLaunchKernelGGL((lora_up_kernel<2>), dim3(g2), dim3(256), lds, s, a);
-  else
-    hipLaunchKernelGGL((lora_up_kernel<1>), dim3(g2), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((lora_up_kernel<NB>), dim3(g2), dim3(256), up_lds(a.rank, NB), s, a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
