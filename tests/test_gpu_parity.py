@@ -84,6 +84,16 @@ def test_small_shapes_full_parity(torch_cuda, case):
     check_accept(w, ds, allow_boundary=0)
 
 
+@pytest.mark.parametrize("V", [2048 * 1024, 2048 * 1024 - 1])
+def test_largest_vocabulary(torch_cuda, V):
+    """The largest vocabulary the acceptance takes (1024 sub-chunks of 2048):
+    every sub-chunk table is full; V - 1 takes the element-wise load path."""
+    w = small(f"vmax{V}", B=6, N=4, Hq=8, Hkv=2, D=64, V=V, ctx=[8, 40, 17, 100, 33, 64],
+              n_drafts=[3, 3, 3, 2, 3, 1])
+    ds = run(w, torch_cuda)
+    check_accept(w, ds, allow_boundary=1)
+
+
 def test_greedy_and_short_draft_lists(torch_cuda):
     w = small("greedy", B=8, N=4, Hq=8, Hkv=2, D=64, V=3001, ctx=[20] * 8, T=0.0,
               n_drafts=[3, 0, 1, 2, 3, 0, 3, 3])
