@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
 def attn_bytes(w):
@@ -58,10 +59,23 @@ def accept_bytes(w, lens, kp):
     return ((rows + 2 * resid) * w.V + bonus * min(2048, w.V)) * es + w.B * (w.N + 1) * 4
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain 1 GiB copy), or None
-    when the kernel sources changed after those counters were taken."""
+def attn_flops(w):
+    """MFMA work of one attention call (2 flops per multiply-add).
+    Algorithmic: Q K^T and P V over the keys each query row sees,
+    4 D Hq sum_b sum_r (ctx_b - R + r + 1).  Issued: every (page, KV head)
+    unit runs both products over full 16-token pages for the query rows padded
+    to 32 per wave (R G rounded up to 32 WR): 2048 D WR flops per unit."""
+    ctx = w.ctx_lens.astype(np.int64)
+    keys = int(sum(int(c) - w.R + r + 1 for c in ctx for r in range(w.R)))
+    algo = 4 * w.D * w.Hq * keys
+    wr = 1 if w.R * (w.Hq // w.Hkv) <= 32 else (2 if w.R * (w.Hq // w.Hkv) <= 64 else 4)
+    units = int(((ctx + 15) // 16).sum()) * w.Hkv
+    return algo, units * 2048 * w.D * wr
+
+
+def _profile_record():
+    """The committed rocprofv3 summary of the attention (HBM counters and MFMA
+    counters), or None when isd_attn.hip changed after they were taken."""
     import hashlib
 
     tfile = os.path.join(ROOT, "profiles", "isd_paged_attn_c64_traffic.json")
@@ -72,7 +86,26 @@ def measured_traffic():
     src = open(os.path.join(csrc, "isd_attn.hip"), "rb").read()
     if hashlib.sha256(src).hexdigest()[:16] != t.get("kernel_source_sha256_16"):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain 1 GiB copy), or None
+    when the kernel sources changed after those counters were taken."""
+    t = _profile_record()
+    return None if t is None else t.get("hbm_bytes_per_launch")
+
+
+def measured_mfma_busy():
+    """Fraction of SIMD cycles the attention stream kernel's MFMA unit was
+    busy (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCD x
+    SIMDs), from the committed summary, or None when stale or absent."""
+    t = _profile_record()
+    if t is None:
+        return None
+    m = t.get("mfma") or {}
+    return next((v["busy_frac"] for k, v in m.items() if k.startswith("attn_stream")), None)
 
 
 def cpu_baseline(w, n_seq, runs):
@@ -355,6 +388,7 @@ def main():
     kp = (w.draft_tokens >= 0).sum(axis=1) if w.N > 1 else np.zeros(w.B, dtype=np.int64)
     committed = int(lens.sum())
     a_bytes = attn_bytes(w)
+    a_flop, i_flop = attn_flops(w)
     c_bytes = accept_bytes(w, lens, kp)
     attn_gbs = a_bytes / (attn_ms * 1e-3) / 1e9
     acc_gbs = c_bytes / (acc_ms * 1e-3) / 1e9
@@ -388,7 +422,13 @@ def main():
         "mean_accept_len": committed / w.B,
         "kernels": {
             "isd_paged_attn": {"ms": attn_ms, **spread(attn_t), "algorithmic_bytes": a_bytes,
-                               "GB/s": attn_gbs, "frac_of_8TB/s": attn_gbs / HBM_PEAK_GBS},
+                               "GB/s": attn_gbs, "frac_of_8TB/s": attn_gbs / HBM_PEAK_GBS,
+                               "mfma": {"algorithmic_TFLOP/s": a_flop / (attn_ms * 1e-3) / 1e12,
+                                        "issued_TFLOP/s": i_flop / (attn_ms * 1e-3) / 1e12,
+                                        "peak_bf16_dense_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
+                                        "frac_algorithmic": a_flop / (attn_ms * 1e-3) / 1e12
+                                        / MFMA_BF16_PEAK_TFLOPS,
+                                        "busy_frac_rocprof": measured_mfma_busy()}},
             "isd_accept": {"ms": acc_ms, **spread(acc_t), "algorithmic_bytes": c_bytes,
                            "GB/s": acc_gbs, "frac_of_8TB/s": acc_gbs / HBM_PEAK_GBS},
         },
