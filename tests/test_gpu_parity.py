@@ -72,6 +72,10 @@ def test_tiny_named_workload(torch_cuda):
     dict(name="d64", B=3, N=4, Hq=8, Hkv=2, D=64, V=4096, ctx=[9, 129, 777]),
     dict(name="wr2", B=2, N=4, Hq=32, Hkv=4, D=128, V=2048, ctx=[50, 1500]),       # 56 rows
     dict(name="n8g8", B=2, N=8, Hq=64, Hkv=8, D=128, V=3000, ctx=[15, 999]),        # 120 rows
+    dict(name="n8g8d64", B=2, N=8, Hq=64, Hkv=8, D=64, V=3000, ctx=[15, 999]),
+    # 120 rows over many short segments: LDS page buffers reused across pairs
+    dict(name="n8g8seg", B=6, N=8, Hq=64, Hkv=8, D=128, V=2000,
+         ctx=[15, 200, 33, 1000, 64, 517]),
     dict(name="n1", B=4, N=1, Hq=32, Hkv=8, D=128, V=5000, ctx=[1, 2, 16, 700]),    # plain decode
     dict(name="f32_128", B=2, N=4, Hq=16, Hkv=4, D=128, V=777, ctx=[7, 500], qkv="f32",
          logits="f32"),
