@@ -116,3 +116,25 @@ def test_rollback_clamps_and_reports():
     assert err == {"bad_len"}
     assert list(c2) == [14, 9]  # accept_len clamped to 1 and 7
     assert n2 == 3 and list(f2[:3]) == [3, 4, 1] and t2[0, 1] == -1
+
+
+def test_stack_order_worked_example():
+    """Hand-worked case (N = 16, R = 31) in which one step takes two pages and
+    the rollback returns both: the free list is a stack, a call takes the top
+    block in order and returns a sequence's pages in page order."""
+    rng = np.random.default_rng(5)
+    R, Hkv, D, dtype = 31, 1, 64, "f32"
+    pool = np.zeros((8, 2, Hkv, 16 * D), dtype=np.float32)
+    table = np.full((1, 4), -1, dtype=np.int32)
+    table[0, 0] = 5                      # ctx 15: page 0 holds tokens 0..14
+    free = np.array([0, 1, 2, 3], dtype=np.int32)
+    k_new, v_new = _rows(rng, 1, R, Hkv, D, dtype), _rows(rng, 1, R, Hkv, D, dtype)
+    pool, table2, ctx, cnt, err = kv_append(pool, table, [15], k_new, v_new, free, 4, dtype)
+    assert not err and list(ctx) == [46] and cnt == 2
+    assert list(table2[0]) == [5, 2, 3, -1]  # the top two entries, in stack order
+    table3, keep, free3, cnt3, err = kv_rollback(table2, ctx, [1], R, free, cnt)
+    assert not err and list(keep) == [16] and cnt3 == 4
+    # keep = 16 tokens = one page: pages 1 and 2 (ids 2, 3) go back in page
+    # order onto the stack positions they were taken from
+    assert list(table3[0]) == [5, -1, -1, -1]
+    assert list(free3) == [0, 1, 2, 3]

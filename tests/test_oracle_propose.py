@@ -4,7 +4,7 @@ import numpy as np
 from scipy import stats
 
 from oracle.accept import isd_accept
-from oracle.philox import philox4x64_10, propose_uniform
+from oracle.philox import MASK64, philox4x64_10, propose_uniform
 from oracle.propose import isd_propose, propose_row
 from oracle.tpf import simulate_chain, tpf_closed_form
 
@@ -97,3 +97,27 @@ def test_proposal_loop_reaches_closed_form():
 
     m = simulate_chain(step, 20_000)
     assert abs(m - tpf_closed_form(a, N)) < 0.05
+
+
+def _numpy_u(counter, key):
+    """Uniform from word 0 of a Philox4x64-10 block, via numpy's own generator
+    (it increments the 256-bit counter before producing a block)."""
+    c = (sum(int(w) << (64 * i) for i, w in enumerate(counter)) - 1) % (1 << 256)
+    bg = np.random.Philox(counter=np.array([(c >> (64 * i)) & MASK64 for i in range(4)],
+                                           dtype=np.uint64),
+                          key=np.array([int(k) & MASK64 for k in key], dtype=np.uint64))
+    return (int(bg.random_raw(4)[0]) >> 40) * 2.0 ** -24
+
+
+def test_draft_i_uses_its_own_counter():
+    """Two equally likely tokens: draft i of sequence b is 1 exactly when its
+    uniform, word 0 of counter (i, 1, 0, 0) under key (seed, b), is >= 1/2
+    (computed here with numpy's Philox), so a shifted stream index fails."""
+    B, K, seed = 4, 7, 123456789
+    logits = np.zeros((B, K, 2))
+    drafts = np.zeros((B, K), dtype=np.int32)
+    out = isd_propose(logits, drafts, np.full(B, K + 1), seed, 1.0)
+    want = np.array([[int(_numpy_u((i, 1, 0, 0), (seed, b)) >= 0.5) for i in range(K)]
+                     for b in range(B)])
+    assert np.array_equal(out, want)
+    assert 0 < want.sum() < want.size  # both tokens occur, so the check has teeth
