@@ -20,9 +20,12 @@
 //              work-groups of the same launch round the verify rows:
 //              bf16(y_base), nothing else.
 //   lora_sum   T = the KS partials summed in share order (float32).
-//   lora_up    MASK rows: T times B^T on float32 MFMA (v_mfma_f32_16x16x4f32,
-//              T and B exact operands), scale * that added to y_base and
-//              rounded once.
+//   lora_up    MASK rows: T times B^T, scale * that added to y_base and
+//              rounded once.  Each float32 T value is split exactly into
+//              three bf16 parts, T = hi + mid + lo (8 + 8 + 8 significant
+//              bits); every part times a bf16 weight is exact in float32, so
+//              three v_mfma_f32_16x16x32_bf16 per 32 ranks accumulate the same
+//              float32 products as float32 MFMA would, at the bf16 rate.
 //
 // Every work-group issues its global loads before it stores anything (stores
 // to y_out could alias y_base as far as the compiler knows), so each launch
@@ -190,12 +193,13 @@ __global__ __launch_bounds__(kSumThreads) void lora_sum_kernel(LoraArgs a) {
   ((float4*)a.t)[i] = sum;
 }
 
-// LDS of a lora_up work-group with NB 16-column blocks per wave: T [16][rank]
-// float32 and B [64 NB][rank] bf16, rows padded by 4 elements (rows stay 16-
-// and 8-byte aligned for vector reads and land on different banks).
-inline size_t up_lds(int rank, int NB) {
-  return (size_t)16 * (rank + 4) * 4 + (size_t)64 * NB * (rank + 4) * 2;
-}
+// LDS of a lora_up work-group with NB 16-column blocks per wave: the three
+// bf16 parts of T [3][16][rank] and B [64 NB][rank] bf16, rows padded by 8
+// elements (16-byte aligned for vector reads, on different banks).
+// Rows hold the ranks rounded up to 32 (the MFMA's k, zero beyond the rank)
+// plus 8 elements of padding.
+inline int up_stride(int rank) { return (rank + 31) / 32 * 32 + 8; }
+inline size_t up_lds(int rank, int NB) { return (size_t)(3 * 16 + 64 * NB) * up_stride(rank) * 2; }
 // One 16-column block per wave (64 columns per work-group): more, smaller
 // work-groups measured faster than 128-column tiles (7.4 vs 8.2 us at
 // M = 448, H = O = 4096, rank 128); LDS stays under 50 KiB up to rank 256.
@@ -226,10 +230,14 @@ __global__ __launch_bounds__(256) void lora_up_kernel(LoraArgs a) {
       yb[c][e] = a.y_base[yo[c][e]];
     }
   }
-  const int tstr = a.rank + 4;  // padded row strides (elements)
-  const int bstr = a.rank + 4;
-  float* sh_t = sh;                              // [16][tstr]
-  uint16_t* sh_b = (uint16_t*)(sh + 16 * tstr);  // [cols][bstr]
+  const int rk = (a.rank + 31) / 32 * 32;   // ranks rounded up to the MFMA's k
+  const int str = rk + 8;                     // padded row stride (elements)
+  uint16_t* sh_t = (uint16_t*)sh;            // [3][16][str]: hi, mid, lo parts of T
+  uint16_t* sh_b = sh_t + 3 * 16 * str;      // [cols][str]
+  if (rk != a.rank) {  // ranks [rank, rk) of every row are zero (16 elements)
+    for (int i = tid; i < (3 * 16 + cols) * 2; i += 256)
+      *(uint4*)(sh_t + (i >> 1) * str + a.rank + 8 * (i & 1)) = make_uint4(0, 0, 0, 0);
+  }
   // T rows (16 x rank float32: at most 4 float4 per thread) and the first
   // 2048 16-byte pieces of the weight rows are loaded together.
   const int r4 = a.rank / 4, rc8 = a.rank / 8;
@@ -255,47 +263,53 @@ __global__ __launch_bounds__(256) void lora_up_kernel(LoraArgs a) {
       for (int u = 0; u < 4; ++u) {
         const int i = u * 256 + tid;
         if (i < 16 * r4) {
-          float* d = sh_t + (i / r4) * tstr + 4 * (i % r4);
-          d[0] = tv[u].x;
-          d[1] = tv[u].y;
-          d[2] = tv[u].z;
-          d[3] = tv[u].w;
+          const float x[4] = {tv[u].x, tv[u].y, tv[u].z, tv[u].w};
+          unsigned part[3][2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // Exact split: each residual is representable, the last part exactly.
+            const uint16_t h = f32_to_bf16_rne(x[e]);
+            const float r1 = x[e] - __uint_as_float((unsigned)h << 16);
+            const uint16_t m = f32_to_bf16_rne(r1);
+            const float r2 = r1 - __uint_as_float((unsigned)m << 16);
+            const uint16_t l = f32_to_bf16_rne(r2);
+            const int sh16 = 16 * (e & 1);
+            if ((e & 1) == 0) part[0][e >> 1] = part[1][e >> 1] = part[2][e >> 1] = 0u;
+            part[0][e >> 1] |= (unsigned)h << sh16;
+            part[1][e >> 1] |= (unsigned)m << sh16;
+            part[2][e >> 1] |= (unsigned)l << sh16;
+          }
+#pragma unroll
+          for (int pp = 0; pp < 3; ++pp)
+            *(uint2*)(sh_t + (pp * 16 + i / r4) * str + 4 * (i % r4)) =
+                make_uint2(part[pp][0], part[pp][1]);
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + u * 256 + tid;
-      if (i < cols * rc8) {
-        uint2* d = (uint2*)(sh_b + (i / rc8) * bstr + 8 * (i % rc8));
-        d[0] = make_uint2(bv[u].x, bv[u].y);
-        d[1] = make_uint2(bv[u].z, bv[u].w);
-      }
+      if (i < cols * rc8) *(uint4*)(sh_b + (i / rc8) * str + 8 * (i % rc8)) = bv[u];
     }
   }
   __syncthreads();
-  // Lane (row, kq) covers ranks [kq r4, (kq + 1) r4): step s multiplies
-  // T[row][kq r4 + s] by B[col][kq r4 + s], so each group of 4 steps reads 4
-  // consecutive floats of T (16 bytes) and 4 bf16 of each B row (8 bytes).
+  // A operand: part of T[row][kk + 8 kq .. + 7]; B operand: B[col][same k].
   f32x4 acc[NB];
 #pragma unroll
   for (int c = 0; c < NB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* tr = sh_t + row * tstr + kq * r4;
-  const uint16_t* br = sh_b + (wave * 16 * NB + row) * bstr + kq * r4;
-  for (int s = 0; s < r4; s += 4) {  // r4 is a multiple of 4
-    const float4 av = *(const float4*)(tr + s);
-    uint2 bq[NB];
+  for (int kk = 0; kk < rk; kk += 32) {
+    const int k = kk + 8 * kq;
+    const bf16x8 th = __builtin_bit_cast(bf16x8, *(const uint4*)(sh_t + (0 * 16 + row) * str + k));
+    const bf16x8 tm = __builtin_bit_cast(bf16x8, *(const uint4*)(sh_t + (1 * 16 + row) * str + k));
+    const bf16x8 tl = __builtin_bit_cast(bf16x8, *(const uint4*)(sh_t + (2 * 16 + row) * str + k));
 #pragma unroll
-    for (int c = 0; c < NB; ++c) bq[c] = *(const uint2*)(br + c * 16 * bstr + s);
-    const float at[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int c = 0; c < NB; ++c) {
-        const unsigned w = (u < 2 ? bq[c].x : bq[c].y) >> (16 * (u & 1));
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(at[u], __uint_as_float(w << 16), acc[c], 0, 0,
-                                                      0);
-      }
+    for (int c = 0; c < NB; ++c) {
+      const bf16x8 bq = __builtin_bit_cast(
+          bf16x8, *(const uint4*)(sh_b + (wave * 16 * NB + c * 16 + row) * str + k));
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, bq, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tm, bq, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, bq, acc[c], 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
