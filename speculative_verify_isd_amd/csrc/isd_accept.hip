@@ -859,10 +859,11 @@ int32_t launch_all(AccArgs a, int U1, hipStream_t s) {
 //                   sub-chunks to (max m_c, sum of exp2((l - m_c) c)) (greedy:
 //                   max, lowest argmax).  Rows of sequences that will not
 //                   continue are skipped, so their logits are never read.
-//   propose_select  grid B*K, one wave per row: weights s_c * 2^((m_c - M) c)
-//                   in sub-chunk order, a wave scan locates the sub-chunk
-//                   holding t = u * total, which is rescanned with the same
-//                   exponentials (relative to m_c) as the stats pass.
+//   propose_select  grid B*K, four waves per row: wave 0 takes the weights
+//                   s_c * 2^((m_c - M) c) in sub-chunk order and a wave scan
+//                   locates the sub-chunk holding t = u * total; all 256
+//                   threads rescan it (8 elements each, a block prefix) with
+//                   the same exponentials (relative to m_c) as the stats pass.
 // ---------------------------------------------------------------------------
 struct PropArgs {
   const void* ln;           // [B][K][V]
@@ -876,7 +877,6 @@ struct PropArgs {
 };
 
 constexpr int kPropSubPerWave = 2;
-constexpr int kSelPer = kSub / 64;  // elements per lane when one wave scans a sub-chunk
 
 // Whether sequence b's next step verifies (all listed drafts kept).
 __device__ inline bool continues(const PropArgs& a, int b) {
@@ -961,18 +961,24 @@ __global__ __launch_bounds__(256) void propose_stats_kernel(PropArgs a) {
 }
 
 template <bool VEC, bool F32>
-__global__ __launch_bounds__(64) void propose_select_kernel(PropArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
+  __shared__ int sh_sc, sh_past, sh_tok;
+  __shared__ double sh_tl;
+  __shared__ float sh_mc;
+  __shared__ double sh_wsum[4];
+  __shared__ int sh_last[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x / a.K, i = blockIdx.x % a.K;
   int32_t* dst = a.next + (size_t)b * a.K + i;
   if (!continues(a, b)) {
-    if (lane == 0) *dst = -1;
+    if (tid == 0) *dst = -1;
     return;
   }
   const double2* st = a.st + ((size_t)b * a.K + i) * a.nsub;
   const int per = (a.nsub + 63) / 64;
   const int k0 = min(a.nsub, lane * per), k1 = min(a.nsub, k0 + per);
   if (a.greedy) {
+    if (wave != 0) return;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
     for (int k = k0; k < k1; ++k) better(bv, bi, (float)st[k].x, (int)st[k].y);
@@ -985,109 +991,125 @@ __global__ __launch_bounds__(64) void propose_select_kernel(PropArgs a) {
     if (lane == 0) *dst = bi == 0x7FFFFFFF ? 0 : bi;
     return;
   }
-  const double c2 = (double)a.c2;
-  double M = -INFINITY;
-  for (int k = k0; k < k1; ++k) M = fmax(M, st[k].x);
+  if (wave == 0) {
+    // Wave 0 locates the sub-chunk: weights s_c 2^((m_c - M) c) in order,
+    // each lane a contiguous run, a wave scan, the first sub-chunk with
+    // positive weight whose end exceeds t = u * W.
+    const double c2 = (double)a.c2;
+    double M = -INFINITY;
+    for (int k = k0; k < k1; ++k) M = fmax(M, st[k].x);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmax(M, __shfl_xor(M, off));
-  // Sub-chunk weights in order; this lane's run sum, then a wave scan.
-  double ls = 0.0;
-  for (int k = k0; k < k1; ++k) {
-    const double2 v = st[k];
-    ls += v.x == -INFINITY ? 0.0 : v.y * exp2((v.x - M) * c2);
+    for (int off = 32; off > 0; off >>= 1) M = fmax(M, __shfl_xor(M, off));
+    double ls = 0.0;
+    for (int k = k0; k < k1; ++k) {
+      const double2 v = st[k];
+      ls += v.x == -INFINITY ? 0.0 : v.y * exp2((v.x - M) * c2);
+    }
+    double inc = ls;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    const double W = __shfl(inc, 63);
+    double ex = __shfl_up(inc, 1);
+    if (lane == 0) ex = 0.0;
+    const double u = top24(philox4x64_10((uint64_t)i, 1, 0, 0, a.seed, (uint64_t)b).w[0]);
+    const double t = u * W;
+    double run = ex, hbase = 0.0, hscale = 0.0;
+    int hit = -1, lastpos = -1;
+    for (int k = k0; k < k1; ++k) {
+      const double2 v = st[k];
+      const double f = v.x == -INFINITY ? 0.0 : exp2((v.x - M) * c2);
+      const double w = v.y * f;
+      if (w > 0.0) lastpos = k;
+      if (hit < 0 && w > 0.0 && run + w > t) {
+        hit = k;
+        hbase = run;
+        hscale = f;
+      }
+      run += w;
+    }
+    const unsigned long long hm = __ballot(hit >= 0);
+    int sc;
+    double tl;  // t relative to the sub-chunk, in its own units (weights relative to m_c)
+    int past = 0;
+    if (hm) {
+      const int src = (int)__builtin_ctzll(hm);
+      sc = __shfl(hit, src);
+      const double base = __shfl(hbase, src), scale = __shfl(hscale, src);
+      tl = fmax(0.0, (t - base) / scale);
+    } else {
+      const unsigned long long pm = __ballot(lastpos >= 0);
+      sc = pm ? __shfl(lastpos, 63 - (int)__builtin_clzll(pm)) : 0;
+      tl = 0.0;
+      past = 1;
+    }
+    if (lane == 0) {
+      sh_sc = sc;
+      sh_tl = tl;
+      sh_past = past;
+      sh_mc = (float)st[sc].x;
+      sh_tok = -1;
+    }
   }
-  double inc = ls;
+  __syncthreads();
+  const int sc = sh_sc, past = sh_past;
+  const double tl = sh_tl;
+  const float mc = sh_mc;
+  // Rescan with all 256 threads: thread t owns elements sc*kSub + 8t .. 8t + 7
+  // (vocabulary order), under a block prefix of the thread sums.
+  const void* row = prop_row(a, b, i);
+  const int v0 = sc * kSub + 8 * tid;
+  const Logits8<VEC, F32> xs = load8<VEC, F32>(row, v0, a.V);
+  float w[8];
+  float part = 0.f;
+  int lastp = -1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = xs[e];
+    w[e] = x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((x - mc) * a.c2);
+    part += w[e];
+    if (w[e] > 0.f) lastp = v0 + e;
+  }
+  double inc = (double)part;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const double y = __shfl_up(inc, off);
     if (lane >= off) inc += y;
   }
-  const double W = __shfl(inc, 63);
+  if (lane == 63) sh_wsum[wave] = inc;
+  const unsigned long long pm = __ballot(lastp >= 0);
+  const int lastw = __shfl(lastp, pm ? 63 - (int)__builtin_clzll(pm) : 0);  // all lanes
+  if (lane == 0) sh_last[wave] = pm ? lastw : -1;
+  __syncthreads();
+  double woff = 0.0;
+  for (int q = 0; q < wave; ++q) woff += sh_wsum[q];
+  inc += woff;
   double ex = __shfl_up(inc, 1);
-  if (lane == 0) ex = 0.0;
-  const double u = top24(philox4x64_10((uint64_t)i, 1, 0, 0, a.seed, (uint64_t)b).w[0]);
-  const double t = u * W;
-  // First sub-chunk with positive weight whose end exceeds t.
-  double run = ex, hbase = 0.0, hscale = 0.0;
-  int hit = -1, lastpos = -1;
-  for (int k = k0; k < k1; ++k) {
-    const double2 v = st[k];
-    const double f = v.x == -INFINITY ? 0.0 : exp2((v.x - M) * c2);
-    const double w = v.y * f;
-    if (w > 0.0) lastpos = k;
-    if (hit < 0 && w > 0.0 && run + w > t) {
-      hit = k;
-      hbase = run;
-      hscale = f;
-    }
-    run += w;
-  }
-  const unsigned long long hm = __ballot(hit >= 0);
-  int sc;
-  double tl;  // t relative to the sub-chunk, in its own units (weights relative to m_c)
-  bool past = false;
-  if (hm) {
-    const int src = (int)__builtin_ctzll(hm);
-    sc = __shfl(hit, src);
-    const double base = __shfl(hbase, src), scale = __shfl(hscale, src);
-    tl = fmax(0.0, (t - base) / scale);
-  } else {
-    const unsigned long long pm = __ballot(lastpos >= 0);
-    sc = pm ? __shfl(lastpos, 63 - (int)__builtin_clzll(pm)) : 0;
-    tl = 0.0;
-    past = true;
-  }
-  const float mc = (float)st[sc].x;
-  // Rescan: lane l owns elements sc*kSub + 32 l .. + 31 (vocabulary order).
-  const void* row = prop_row(a, b, i);
-  const int v0 = sc * kSub + kSelPer * lane;
-  Logits8<VEC, F32> xs[kSelPer / 8];
-#pragma unroll
-  for (int g = 0; g < kSelPer / 8; ++g) xs[g] = load8<VEC, F32>(row, v0 + 8 * g, a.V);
-  float w[kSelPer];
-  double ll = 0.0;
-  int lastp = -1;
-#pragma unroll
-  for (int g = 0; g < kSelPer / 8; ++g) {
-    float part = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = xs[g][e];
-      w[8 * g + e] = x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((x - mc) * a.c2);
-      part += w[8 * g + e];
-      if (w[8 * g + e] > 0.f) lastp = v0 + 8 * g + e;
-    }
-    ll += (double)part;
-  }
-  double li = ll;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(li, off);
-    if (lane >= off) li += y;
-  }
-  double le = __shfl_up(li, 1);
-  if (lane == 0) le = 0.0;
-  const bool holder = !past && le <= tl && tl < li;
-  int tok = lastp;
-  if (holder) {
-    double r = le;
+  if (lane == 0) ex = woff;
+  // [ex, inc): consecutive threads share end points exactly, so at most one
+  // thread holds tl.
+  if (!past && ex <= tl && tl < inc) {
+    double r = ex;
+    int tok = lastp;
     bool done = false;
 #pragma unroll
-    for (int e = 0; e < kSelPer; ++e) {
+    for (int e = 0; e < 8; ++e) {
       r += (double)w[e];
       if (!done && r > tl) {
         tok = v0 + e;
         done = true;
       }
     }
+    sh_tok = tok;
   }
-  const unsigned long long hm2 = __ballot(holder);
-  const unsigned long long pm2 = __ballot(lastp >= 0);
-  if (hm2)
-    tok = __shfl(tok, (int)__builtin_ctzll(hm2));
-  else
-    tok = pm2 ? __shfl(lastp, 63 - (int)__builtin_clzll(pm2)) : min(a.V - 1, sc * kSub);
-  if (lane == 0) *dst = tok;
+  __syncthreads();
+  if (tid == 0) {
+    int tok = sh_tok;
+    for (int q = 3; q >= 0 && tok < 0; --q) tok = sh_last[q];
+    *dst = tok < 0 ? min(a.V - 1, sc * kSub) : tok;
+  }
 }
 
 template <bool VEC, bool F32>
@@ -1097,7 +1119,7 @@ int32_t launch_propose_t(PropArgs a, hipStream_t s) {
   const int64_t g1 = (int64_t)a.B * a.K * S;
   hipLaunchKernelGGL((propose_stats_kernel<VEC, F32>), dim3((unsigned)g1), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
-  hipLaunchKernelGGL((propose_select_kernel<VEC, F32>), dim3((unsigned)(a.B * a.K)), dim3(64), 0,
+  hipLaunchKernelGGL((propose_select_kernel<VEC, F32>), dim3((unsigned)(a.B * a.K)), dim3(256), 0,
                      s, a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
