@@ -66,6 +66,7 @@ struct AttnArgs {
   int32_t* status;
   int B, R, Hq, Hkv, G, RG, D, max_pages, num_pages;
   int nlanes;       // wave-lanes of the streaming grid
+  int mslices;      // merge work-groups per pair: 1, or one per kMergeRows query rows
   float scale_log2;  // log2(e) / sqrt(D)
 };
 
@@ -456,8 +457,111 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
   if (u < uend) walk(u, uend, (size_t)wl * 2);
 }
 
+constexpr int kMergeRows = 8;  // query rows of a merge slice
+
+// Folds rows [r0, r0 + kMergeRows) of a split pair's pieces (collective over
+// the work-group): every piece's (max, sum) for those rows, then the partial
+// outputs in unit order, kSBatch pieces' loads at a time.
+template <int D, int ROWS>
+__device__ void merge_slice(const AttnArgs& a, int b, int h, int r0, int npieces, int wa,
+                            int64_t start, int64_t span) {
+  constexpr int D4 = D / 4;
+  constexpr int kSVec = (kMergeRows * D4 + 255) / 256;  // float4 outputs per thread
+  constexpr int kSBatch = 16 / kSVec;
+  __shared__ float sm_M[kMergeRows], sm_iL[kMergeRows];
+  __shared__ float sm_f[kSBatch][kMergeRows];
+  const int tid = threadIdx.x;
+  const int nrows = min(kMergeRows, a.RG - r0);
+  const int nvec = nrows * D4;
+  auto slot_of = [&](int k) -> size_t {
+    return (size_t)(wa + k) * 2 + ((k == 0 && start != (int64_t)wa * span) ? 1 : 0);
+  };
+  auto load_batch = [&](int k0, float4 (&v)[kSBatch][kSVec]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kSBatch; ++t) {
+      const int k = min(k0 + t, npieces - 1);  // clamped, unconditional
+      const float4* po = (const float4*)(a.part_o + (slot_of(k) * ROWS + r0) * D);
+#pragma unroll
+      for (int e = 0; e < kSVec; ++e) v[t][e] = po[min(tid + 256 * e, nvec - 1)];
+    }
+  };
+  float4 v[kSBatch][kSVec];
+  load_batch(0, v);
+  if (tid < nrows) {
+    // Row maxima and normalisers, 16 pieces' loads in flight at a time
+    // (clamped, unconditional), summed in unit order.
+    const int row = r0 + tid;
+    float M = -INFINITY;
+    for (int k0 = 0; k0 < npieces; k0 += 16) {
+      float mx[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx[j] = a.part_ml[slot_of(min(k0 + j, npieces - 1)) * ROWS + row].x;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (k0 + j < npieces) M = fmaxf(M, mx[j]);
+    }
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+    for (int k0 = 0; k0 < npieces; k0 += 16) {
+      float2 ml[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ml[j] = a.part_ml[slot_of(min(k0 + j, npieces - 1)) * ROWS + row];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (k0 + j < npieces) L += ml[j].y * exp2f(ml[j].x - Mu);
+    }
+    sm_M[tid] = Mu;
+    sm_iL[tid] = 1.f / L;
+  }
+  float4 O[kSVec];
+#pragma unroll
+  for (int e = 0; e < kSVec; ++e) O[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < npieces; k0 += kSBatch) {
+    __syncthreads();  // (M, 1/L) written; the previous batch's factors consumed
+    if (k0 > 0) load_batch(k0, v);
+    if (tid < nrows) {
+      const float Mu = sm_M[tid], iL = sm_iL[tid];
+#pragma unroll
+      for (int t = 0; t < kSBatch; ++t)
+        sm_f[t][tid] = k0 + t < npieces
+                           ? exp2f(a.part_ml[slot_of(k0 + t) * ROWS + r0 + tid].x - Mu) * iL
+                           : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kSBatch; ++t)
+#pragma unroll
+      for (int e = 0; e < kSVec; ++e) {
+        const int i = min(tid + 256 * e, nvec - 1);
+        const float f = sm_f[t][i / D4];
+        O[e].x += v[t][e].x * f;
+        O[e].y += v[t][e].y * f;
+        O[e].z += v[t][e].z * f;
+        O[e].w += v[t][e].w * f;
+      }
+  }
+  u16* outp = (u16*)a.out;
+#pragma unroll
+  for (int e = 0; e < kSVec; ++e) {
+    const int i = tid + 256 * e;
+    if (i < nvec) {
+      const int row = r0 + i / D4, d = 4 * (i % D4);
+      const int r = row / a.G, g = row % a.G;
+      const unsigned lo = f32_to_bf16_rne(O[e].x) | ((unsigned)f32_to_bf16_rne(O[e].y) << 16);
+      const unsigned hi = f32_to_bf16_rne(O[e].z) | ((unsigned)f32_to_bf16_rne(O[e].w) << 16);
+      *(uint2*)(outp + (((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D + d) =
+          make_uint2(lo, hi);
+    }
+  }
+}
+
 // Combines the pieces of (b, h) pairs that were split across wave-lane runs,
-// in unit order.  One work-group per pair; pairs written whole by one run
+// in unit order.  a.mslices work-groups per pair: with one, the pair is
+// folded whole, kBatch pieces' loads at a time; with one per slice of
+// kMergeRows query rows (chosen when few pairs are spread over many runs), a
+// pair of more than kBatch pieces is folded slice by slice, so several
+// compute units share its pieces, and a pair of at most kBatch pieces is
+// still folded whole by its first work-group.  Pairs written whole by one run
 // exit at once.
 template <int D, int WR>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
@@ -469,7 +573,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   __shared__ float sh_M[ROWS], sh_iL[ROWS];
   __shared__ float sh_f[kBatch][ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int pair = blockIdx.x;
+  const int pair = blockIdx.x / a.mslices, slice = blockIdx.x % a.mslices;
   const int b = pair / a.Hkv, h = pair % a.Hkv;
 
   // Units before sequence b and in the whole batch.
@@ -504,6 +608,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   auto slot_of = [&](int k) -> size_t {
     return (size_t)(wa + k) * 2 + ((k == 0 && start != (int64_t)wa * span) ? 1 : 0);
   };
+  if (npieces > kBatch && a.mslices > 1) {
+    if (kMergeRows * slice < a.RG)
+      merge_slice<D, ROWS>(a, b, h, kMergeRows * slice, npieces, wa, start, span);
+    return;
+  }
+  if (slice != 0) return;
   // Each thread owns up to kMergeVec 4-wide d groups of the R*G x D output.
   // The first kBatch pieces' partial outputs are loaded before anything
   // waits, together with the pieces' (max, sum) rows, so a pair of up to
@@ -688,7 +798,12 @@ int32_t launch_stream(AttnArgs a, hipStream_t s) {
   a.nlanes = grid * (4 / WR);
   hipLaunchKernelGGL((attn_stream_kernel<D, WR>), dim3(grid), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
-  hipLaunchKernelGGL((attn_merge_kernel<D, WR>), dim3(a.B * a.Hkv), dim3(256), 0, s, a);
+  // Slices only while they fit in one round of resident work-groups (two per
+  // CU): otherwise every early-exiting slice costs a round of its own.
+  const int slices = 32 * WR / kMergeRows;
+  a.mslices = (int64_t)a.B * a.Hkv * slices <= 2 * 256 ? slices : 1;
+  hipLaunchKernelGGL((attn_merge_kernel<D, WR>), dim3(a.B * a.Hkv * a.mslices), dim3(256), 0, s,
+                     a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
@@ -718,6 +833,7 @@ int32_t launch_paged_attn(const idlm_isd_dims& d, const Plan& p, const void* q, 
   a.max_pages = d.max_pages;
   a.num_pages = d.num_pages;
   a.nlanes = 0;
+  a.mslices = 1;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d.D));
   if (d.qkv_dtype == IDLM_F32) {
     if (d.D == 64)
