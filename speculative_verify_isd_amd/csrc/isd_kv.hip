@@ -165,16 +165,19 @@ __global__ __launch_bounds__(kPlanThreads) void kv_append_plan_kernel(KvArgs a) 
 // chunk(s), V to the transposed block.
 template <bool F32>
 __global__ __launch_bounds__(256) void kv_scatter_kernel(KvArgs a) {
+  // Thread order (b, h, g, r), r fastest: a step's rows sit in consecutive
+  // slots of a page, so neighbouring threads write neighbouring K chunks
+  // (16 bytes apart) and neighbouring V elements of each transposed d row.
   const int G8 = a.D / 8;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t n = (int64_t)a.B * a.R * a.Hkv * G8;
   if (i >= n) return;
-  const int g = (int)(i % G8);
-  int64_t t = i / G8;
+  const int r = (int)(i % a.R);
+  int64_t t = i / a.R;
+  const int g = (int)(t % G8);
+  t /= G8;
   const int h = (int)(t % a.Hkv);
-  t /= a.Hkv;
-  const int r = (int)(t % a.R);
-  const int b = (int)(t / a.R);
+  const int b = (int)(t / a.Hkv);
   if (!a.valid[b]) return;
   const int64_t pos = (int64_t)a.ctx_out[b] - a.R + r;
   const int page = a.page_table[(size_t)b * a.max_pages + pos / kPage];
