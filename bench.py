@@ -63,14 +63,15 @@ def attn_flops(w):
     """MFMA work of one attention call (2 flops per multiply-add).
     Algorithmic: Q K^T and P V over the keys each query row sees,
     4 D Hq sum_b sum_r (ctx_b - R + r + 1).  Issued: every (page, KV head)
-    unit runs both products over full 16-token pages for the query rows padded
-    to 32 per wave (R G rounded up to 32 WR): 2048 D WR flops per unit."""
+    unit runs both products over full 16-token pages for the query rows of a
+    run (R G padded to 32, 64 or 128): 64 D rows flops per unit."""
     ctx = w.ctx_lens.astype(np.int64)
     keys = int(sum(int(c) - w.R + r + 1 for c in ctx for r in range(w.R)))
     algo = 4 * w.D * w.Hq * keys
-    wr = 1 if w.R * (w.Hq // w.Hkv) <= 32 else (2 if w.R * (w.Hq // w.Hkv) <= 64 else 4)
+    rg = w.R * (w.Hq // w.Hkv)
+    rows = 32 if rg <= 32 else (64 if rg <= 64 else 128)
     units = int(((ctx + 15) // 16).sum()) * w.Hkv
-    return algo, units * 2048 * w.D * wr
+    return algo, units * 64 * w.D * rows
 
 
 def _profile_record(w):

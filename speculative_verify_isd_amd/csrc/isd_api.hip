@@ -46,8 +46,11 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   a.R = 2 * d.N - 1;
   a.G = d.Hq / d.Hkv;
   a.RG = a.R * a.G;
-  a.WR = a.RG <= 32 ? 1 : (a.RG <= 64 ? 2 : 4);
-  a.RGp = 32 * a.WR;
+  // 16-row MFMA blocks per wave and waves per run: one wave of 32 or 64
+  // rows, else two waves of 64 rows walking the same run.
+  a.RB = a.RG <= 32 ? 2 : 4;
+  a.WR = a.RG <= 64 ? 1 : 2;
+  a.RGp = 16 * a.RB * a.WR;
   a.npairs = d.B * d.Hkv;
   a.max_lanes = kMaxWaves / a.WR;
   // ---- acceptance ----

@@ -21,18 +21,20 @@
 //   boundaries depend only on the sizes, so results do not depend on timing.
 //
 //   All R*G query rows of a pair share every K/V page, so each page is read
-//   once and reused across the query tile: a wave carries 32 query rows (two
-//   16-row MFMA blocks, rows r*G + g on the MFMA N side).  For R*G > 32,
-//   WR = 2 or 4 waves of a work-group walk the same run, one 32-row group
-//   each; otherwise the 4 waves are 4 independent lanes.
+//   once and reused across the query tile: a wave carries RB 16-row MFMA
+//   blocks (rows r*G + g on the MFMA N side): 32 rows for R*G <= 32, else
+//   64.  For R*G > 64, WR = 2 waves of a work-group walk the same run, one
+//   64-row group each; otherwise the 4 waves are 4 independent lanes.  The
+//   HBM rate follows the number of independent runs, so rows go to as few
+//   waves per run as the registers allow.
 //
 //   Per page (16 tokens) and 16-row block a wave runs
 //     S^T[tok][row] = K[tok][:] . Q[row][:]   (D/32 x mfma_f32_16x16x32_bf16)
-//     online softmax on S^T (rows in lanes, tokens in registers)
+//     weights 2^(S c - m) against the segment's reference max m
 //     O^T[d][row]  += V^T[d][tok] . P^T[tok][row]  (D/16 x mfma_f32_16x16x16_bf16)
 //   The S^T accumulator layout is exactly the B-operand layout P^T needs,
-//   and O^T keeps rows in lanes, so the softmax needs no data movement
-//   beyond two row-swap permutes for the max.
+//   and O^T keeps rows in lanes, so the softmax moves no data except two
+//   row-swap permutes for the first page's max.
 //
 //   The page layout is chosen for these operands: each K fragment load is a
 //   contiguous 1 KiB per wave (16 B per lane) and each V^T fragment load a
@@ -123,20 +125,25 @@ struct PageFrag {
 
 // Issue one page's loads.  K: one contiguous 1 KiB per 32-wide d step (16 B
 // per lane); V^T: one contiguous 512 B per 16-wide d block (8 B per lane).
-// Every KV byte is read once per step, so the loads are non-temporal: on
-// gfx950 that streams them past the caches and sustains ~13% more HBM
-// bandwidth than ordinary loads.
-template <int D>
+// A page read by one wave only is read once per step, so those loads are
+// non-temporal (NT): on gfx950 that streams them past the caches and
+// sustains ~13% more HBM bandwidth than ordinary loads.  When two waves
+// share a run each page is read twice, close together; ordinary loads let
+// the second read hit in L2 (non-temporal ones fetched ~9% more from HBM).
+template <int D, bool NT>
 __device__ inline void load_page(PageFrag<D>& f, const u16* kv, size_t v_off, int lane) {
   constexpr int NC = D / 32, ND = D / 16;
   const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    f.k[c] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(kv + 512 * c + 8 * lane)));
+  for (int c = 0; c < NC; ++c) {
+    const u32x4* pk = (const u32x4*)(kv + 512 * c + 8 * lane);
+    f.k[c] = __builtin_bit_cast(bf16x8, NT ? __builtin_nontemporal_load(pk) : *pk);
+  }
 #pragma unroll
-  for (int j = 0; j < ND; ++j)
-    f.v[j] = __builtin_bit_cast(
-        s16x4, __builtin_nontemporal_load((const u32x2*)(kv + v_off + (size_t)(16 * j + col) * kPage + 4 * grp)));
+  for (int j = 0; j < ND; ++j) {
+    const u32x2* pv = (const u32x2*)(kv + v_off + (size_t)(16 * j + col) * kPage + 4 * grp);
+    f.v[j] = __builtin_bit_cast(s16x4, NT ? __builtin_nontemporal_load(pv) : *pv);
+  }
 }
 
 // Max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with
@@ -150,71 +157,116 @@ __device__ inline float max_over_rows(float v) {
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
-// Online-softmax rescaling is lazy: the running max (log2 units) is raised
-// only when a new score exceeds it by more than kLazyTau, so between raises
-// the weights stay below 2^kLazyTau and the accumulators are not touched.
-// The final normalisation uses the same running max, so this is exact.
-constexpr float kLazyTau = 8.0f;
+// The softmax of a segment is taken against a fixed reference max per row
+// (log2 units): the row max of the segment's first page.  Later pages never
+// rescale the accumulators (a rescale branch in the page loop costs register
+// copies on every page), so a weight 2^(s - m) exceeds 1 when a later score
+// beats the first page.  A lane whose partial row sum passes 2^kRefSlack
+// (which every weight that large forces) sends the segment to a slow path: a
+// sweep for the true row max, then the segment again with that max as the
+// reference, where no weight exceeds 1.  Below that bound no weight, sum or
+// accumulator can overflow, and the final normalisation and the merge use
+// the same reference, so the result does not depend on which one was taken.
+constexpr float kRefSlack = 24.0f;
+constexpr float kRefBound = 16777216.0f;  // 2^kRefSlack
 
-// One page (16 tokens) for this wave's two 16-row blocks: S^T = K Q^T
-// (mfma 16x16x32), online softmax in exp2 space, O^T += V^T P^T (mfma
-// 16x16x16: the S^T accumulator is already P^T's B-operand layout).  MASKED
-// applies the causal mask (and masks a padding step entirely when !has).
-template <int D, bool MASKED>
-__device__ inline void compute_page(const PageFrag<D>& f, const bf16x8* qs, int lane,
-                                    const int (&pos)[2], int t, bool has, float c2,
-                                    float (&m)[2], float (&l)[2], f32x4 (&acc)[2][D / 16]) {
-  constexpr int NC = D / 32, ND = D / 16;
+__device__ inline float max4(const f32x4& v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
+
+// S^T = K Q^T of one page for the 16-row blocks h0, h0 + 1 (mfma
+// 16x16x32).  MASKED sets the scores of tokens past a row's position (all
+// of them when !has, a padding step) to -inf.
+template <int D, int RB, bool MASKED>
+__device__ inline void scores_pair(const PageFrag<D>& f, const bf16x8* qs, int lane, int h0,
+                                   const int (&pos)[RB], int t, bool has, f32x4 (&sc)[2]) {
+  constexpr int NC = D / 32;
   // Query fragments come from this wave's LDS copy (registers are kept for
   // the K/V pipeline).
   bf16x8 qf[2][NC];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[rb][c] = qs[(rb * NC + c) * 64 + lane];
-  f32x4 sc[2];
+    for (int c = 0; c < NC; ++c) qf[i][c] = qs[((h0 + i) * NC + c) * 64 + lane];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) sc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 2; ++i) sc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-      sc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[c], qf[rb][c], sc[rb], 0, 0, 0);
+    for (int i = 0; i < 2; ++i)
+      sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[c], qf[i][c], sc[i], 0, 0, 0);
+  if (MASKED) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[i][e] = (has && t + e <= pos[h0 + i]) ? sc[i][e] : -INFINITY;
+  }
+}
 
-  float mx[2];
+// Weights p = 2^(s c2 - m) of the blocks h0, h0 + 1, their row sums, and
+// O^T += V^T P^T (mfma 16x16x16: the S^T accumulator is already P^T's
+// B-operand layout).
+template <int D, int RB>
+__device__ inline void accumulate_pair(const PageFrag<D>& f, int h0, const f32x4 (&sc)[2],
+                                       float c2, const float (&mneg)[RB], float (&l)[RB],
+                                       f32x4 (&acc)[RB][D / 16]) {
+  constexpr int ND = D / 16;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    if (MASKED) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[rb][e] = (has && t + e <= pos[rb]) ? sc[rb][e] : -INFINITY;
-    }
-    const float v = fmaxf(fmaxf(sc[rb][0], sc[rb][1]), fmaxf(sc[rb][2], sc[rb][3]));
-    mx[rb] = max_over_rows(v) * c2;
-  }
-  if (__any((mx[0] > m[0] + kLazyTau) || (mx[1] > m[1] + kLazyTau))) {
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float mnew = fmaxf(m[rb], mx[rb]);
-      const float alpha = __builtin_amdgcn_exp2f(m[rb] - (mnew == -INFINITY ? 0.f : mnew));
-      m[rb] = mnew;
-      l[rb] *= alpha;
-#pragma unroll
-      for (int j = 0; j < ND; ++j) acc[rb][j] *= alpha;
-    }
-  }
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float mneg = (m[rb] == -INFINITY) ? 0.f : -m[rb];
+  for (int i = 0; i < 2; ++i) {
+    const int rb = h0 + i;
     float p[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[rb][e], c2, mneg));
+    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[i][e], c2, mneg[rb]));
     l[rb] += (p[0] + p[1]) + (p[2] + p[3]);
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const bf16x4 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-    const s16x4 pf = __builtin_bit_cast(s16x4, pb);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 lo = __builtin_convertvector((f32x2){p[0], p[1]}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector((f32x2){p[2], p[3]}, bf16x2);
+    const s16x4 pf = __builtin_bit_cast(s16x4, (u32x2){__builtin_bit_cast(unsigned, lo),
+                                                        __builtin_bit_cast(unsigned, hi)});
 #pragma unroll
     for (int j = 0; j < ND; ++j)
       acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(f.v[j], pf, acc[rb][j], 0, 0, 0);
+  }
+}
+
+// One page (16 tokens) for all RB row blocks of this wave, two blocks at a
+// time (a scheduling barrier between the pairs keeps their temporaries from
+// being live together, so 64-row waves fit in registers at D = 128).  FIRST
+// marks a segment's first page: with set_ref it takes the rows' max over
+// this page as the reference m (mneg = -m, or 0 for a row with nothing
+// visible).
+template <int D, int RB, bool MASKED, bool FIRST>
+__device__ inline void compute_page(const PageFrag<D>& f, const bf16x8* qs, int lane,
+                                    const int (&pos)[RB], int t, bool has, float c2, bool set_ref,
+                                    float (&m)[RB], float (&mneg)[RB], float (&l)[RB],
+                                    f32x4 (&acc)[RB][D / 16]) {
+  static_assert(RB % 2 == 0, "row blocks go in pairs");
+#pragma unroll
+  for (int h0 = 0; h0 < RB; h0 += 2) {
+    if (h0 > 0) __builtin_amdgcn_sched_barrier(0);
+    f32x4 sc[2];
+    scores_pair<D, RB, MASKED>(f, qs, lane, h0, pos, t, has, sc);
+    if (FIRST && set_ref) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rb = h0 + i;
+        m[rb] = max_over_rows(max4(sc[i])) * c2;
+        mneg[rb] = m[rb] == -INFINITY ? 0.f : -m[rb];
+      }
+    }
+    accumulate_pair<D, RB>(f, h0, sc, c2, mneg, l, acc);
+  }
+}
+
+// Slow path: the lane-local max of one page's raw scores, folded into mloc.
+template <int D, int RB, bool MASKED>
+__device__ inline void max_page(const PageFrag<D>& f, const bf16x8* qs, int lane,
+                                const int (&pos)[RB], int t, bool has, float (&mloc)[RB]) {
+#pragma unroll
+  for (int h0 = 0; h0 < RB; h0 += 2) {
+    f32x4 sc[2];
+    scores_pair<D, RB, MASKED>(f, qs, lane, h0, pos, t, has, sc);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) mloc[h0 + i] = fmaxf(mloc[h0 + i], max4(sc[i]));
   }
 }
 
@@ -270,19 +322,20 @@ __device__ inline int64_t run_length(int64_t total, int nlanes) {
 // ---------------------------------------------------------------------------
 // bf16 streaming kernel
 // ---------------------------------------------------------------------------
-template <int D, int WR>
+template <int D, int WR, int RB>
 __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
   constexpr int kRing = D == 128 ? kRingPages : kRingPages + 2;  // page buffers per wave
   constexpr int NC = D / 32;  // K-dim steps of the QK product
   constexpr int ND = D / 16;  // 16-wide d blocks of the PV product
   constexpr int WK = 4 / WR;  // independent lanes per work-group
-  constexpr int ROWS = 32 * WR;
+  constexpr int WROWS = 16 * RB;  // query rows of one wave
+  constexpr int ROWS = WROWS * WR;  // query rows of a run
 
-  __shared__ bf16x8 lds_q[4][2 * NC * 64];  // each wave's query fragments
+  __shared__ bf16x8 lds_q[4][RB * NC * 64];  // each wave's query fragments
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rgrp = wave % WR;  // 32-row group of this wave
+  const int rgrp = wave % WR;  // row group of this wave within its run
   const int wl = blockIdx.x * WK + wave / WR;  // this wave-lane
   bf16x8* qs = lds_q[wave];
   const int col = lane & 15, grp = lane >> 4;
@@ -300,21 +353,22 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
   const size_t v_off = (size_t)a.Hkv * kPage * D;
   u16* outp = (u16*)a.out;
 
-  float m[2], l[2];
-  f32x4 acc[2][ND];
+  float m[RB], l[RB];
+  f32x4 acc[RB][ND];
 
   // Streams pages [p0, p1) of pair (b, h) into (m, l, acc), starting from an
-  // empty state.
+  // empty state: m is the softmax reference (log2 units), l and acc are
+  // relative to it.
   auto stream = [&](int b, int h, int ctx, int p0, int p1) __attribute__((always_inline)) {
     const size_t head_off = (size_t)h * kPage * D;
     const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
     // Query fragments (B operand of S^T = K Q^T): row = lane's column, eight
     // consecutive d per lane; k-step c covers d chunk 4c + grp.  Staged in
     // this wave's LDS slot; a wave's own LDS accesses stay in order.
-    int pos[2];
+    int pos[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int i = rgrp * 32 + rb * 16 + col;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = rgrp * WROWS + rb * 16 + col;
       const bool valid = i < a.RG;
       const int r = valid ? i / a.G : a.R - 1;
       const int g = valid ? i % a.G : 0;
@@ -327,57 +381,104 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
         qs[(rb * NC + c) * 64 + lane] = __builtin_bit_cast(bf16x8, v);
       }
     }
+    const float c2 = a.scale_log2;
+    float mneg[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       m[rb] = -INFINITY;
+      mneg[rb] = 0.f;
       l[rb] = 0.f;
 #pragma unroll
       for (int j = 0; j < ND; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int cnt = p1 - p0;
-    if (cnt > 0) {
-      // One page per step through a ring of kRing register buffers: kRing-1
-      // pages are in flight while one computes.  Every prefetch is issued
-      // unconditionally (so the compiler waits for exactly one buffer at a
-      // time); prefetches past the end re-read the last page (a cache hit)
-      // and their compute is fully masked.  The scheduling barriers keep
-      // each prefetch ahead of the compute it must overlap.
-      const int last = cnt - 1;
-      const int nrun = ((cnt + kRing - 1) / kRing) * kRing;
-      const int minpos = ctx - a.R;  // every row sees tokens up to here
-      auto issue = [&](PageFrag<D>& f, int st) __attribute__((always_inline)) {
-        const int pg = p0 + min(st, last);
-        int id = sload(pt, pg);
-        if ((unsigned)id >= (unsigned)a.num_pages) {
-          flag(a.status, kBadPage);
-          id = 0;
+    // One page per step through a ring of kRing register buffers: kRing-1
+    // pages are in flight while one computes.  Every prefetch is issued
+    // unconditionally (so the compiler waits for exactly one buffer at a
+    // time); prefetches past the end re-read the last page (a cache hit) and
+    // their compute is fully masked.  The scheduling barriers keep each
+    // prefetch ahead of the compute it must overlap.  Page q sits in buffer
+    // q % kRing.
+    const int last = cnt - 1;
+    const int nrun = 1 + ((cnt - 1 + kRing - 1) / kRing) * kRing;  // steps, first page included
+    const int minpos = ctx - a.R;  // every row sees tokens up to here
+    auto issue = [&](PageFrag<D>& f, int st) __attribute__((always_inline)) {
+      const int pg = p0 + min(st, last);
+      int id = sload(pt, pg);
+      if ((unsigned)id >= (unsigned)a.num_pages) {
+        flag(a.status, kBadPage);
+        id = 0;
+      }
+      load_page<D, (WR == 1)>(f, kvb + (size_t)id * page_elems + head_off, v_off, lane);
+    };
+    // Pass 0 takes its reference from the first page; pass 1 (the slow path)
+    // runs only after a max sweep has set the reference to the true row max.
+    for (int pass = 0; pass < 2 && cnt > 0; ++pass) {
+      const bool set_ref = pass == 0;
+      if (pass == 1) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          l[rb] = 0.f;
+#pragma unroll
+          for (int j = 0; j < ND; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        load_page<D>(f, kvb + (size_t)id * page_elems + head_off, v_off, lane);
-      };
+      }
       auto run = [&](const PageFrag<D>& f, int st) __attribute__((always_inline)) {
         const int t0 = (p0 + st) * kPage;
         const bool has = st < cnt;
         if (has && t0 + kPage - 1 <= minpos)
-          compute_page<D, false>(f, qs, lane, pos, t0 + 4 * grp, true, a.scale_log2, m, l, acc);
+          compute_page<D, RB, false, false>(f, qs, lane, pos, t0 + 4 * grp, true, c2, false, m,
+                                            mneg, l, acc);
         else
-          compute_page<D, true>(f, qs, lane, pos, t0 + 4 * grp, has, a.scale_log2, m, l, acc);
+          compute_page<D, RB, true, false>(f, qs, lane, pos, t0 + 4 * grp, has, c2, false, m,
+                                           mneg, l, acc);
       };
       PageFrag<D> ring[kRing];
 #pragma unroll
-      for (int i = 0; i < kRing - 1; ++i) issue(ring[i], i);
-      for (int st = 0; st < nrun; st += kRing) {
+      for (int i = 0; i < kRing; ++i) issue(ring[i], i);
+      __builtin_amdgcn_sched_barrier(0);
+      {  // the first page sets the reference
+        const int t0 = p0 * kPage;
+        if (t0 + kPage - 1 <= minpos)
+          compute_page<D, RB, false, true>(ring[0], qs, lane, pos, t0 + 4 * grp, true, c2, set_ref,
+                                           m, mneg, l, acc);
+        else
+          compute_page<D, RB, true, true>(ring[0], qs, lane, pos, t0 + 4 * grp, true, c2, set_ref,
+                                          m, mneg, l, acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      for (int st = 1; st < nrun; st += kRing) {
 #pragma unroll
         for (int i = 0; i < kRing; ++i) {
-          issue(ring[(i + kRing - 1) % kRing], st + i + kRing - 1);
+          issue(ring[i], st + i + kRing - 1);
           __builtin_amdgcn_sched_barrier(0);
-          run(ring[i], st + i);
+          run(ring[(i + 1) % kRing], st + i);
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      bool over = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) over = over || !(l[rb] <= kRefBound);
+      if (pass == 1 || !__any(over)) break;
+      // Slow path: the true row max of the segment, then the segment again.
+      float mloc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) mloc[rb] = -INFINITY;
+      for (int st = 0; st < cnt; ++st) {
+        PageFrag<D> f;
+        issue(f, st);
+        const int t0 = (p0 + st) * kPage;
+        max_page<D, RB, true>(f, qs, lane, pos, t0 + 4 * grp, true, mloc);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        m[rb] = max_over_rows(mloc[rb]) * c2;
+        mneg[rb] = m[rb] == -INFINITY ? 0.f : -m[rb];
       }
     }
     // Row sums: every lane holds a partial over its tokens.
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       l[rb] += __shfl_xor(l[rb], 16);
       l[rb] += __shfl_xor(l[rb], 32);
     }
@@ -386,8 +487,8 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
   // Final rows of pair (b, h): lane holds O^T[16j + 4grp + e][row col].
   auto write_out = [&](int b, int h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int i = rgrp * 32 + rb * 16 + col;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = rgrp * WROWS + rb * 16 + col;
       if (i < a.RG) {
         const int r = i / a.G, g = i % a.G;
         const float il = 1.f / l[rb];
@@ -406,8 +507,8 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
   // Softmax state of a piece of a pair, for attn_merge_kernel.
   auto write_part = [&](size_t slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int row = rgrp * 32 + rb * 16 + col;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = rgrp * WROWS + rb * 16 + col;
       float* po = a.part_o + (slot * ROWS + row) * D + 4 * grp;
 #pragma unroll
       for (int j = 0; j < ND; ++j)
@@ -563,9 +664,8 @@ __device__ void merge_slice(const AttnArgs& a, int b, int h, int r0, int npieces
 // compute units share its pieces, and a pair of at most kBatch pieces is
 // still folded whole by its first work-group.  Pairs written whole by one run
 // exit at once.
-template <int D, int WR>
+template <int D, int ROWS>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int ROWS = 32 * WR;
   constexpr int kMergeVec = (ROWS * D / 4 + 255) / 256;  // float4 outputs per thread
   constexpr int kBatch = kMergeVec < 32 ? 32 / kMergeVec : 1;  // pieces loaded together
   constexpr int kMlHeld = kBatch < 8 ? 8 : kBatch;  // pieces' (max, sum) a row thread holds
@@ -770,7 +870,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 // Work-groups the streaming kernel keeps resident on this device (queried
 // once per device): every CU times the kernel's occupancy.
-template <int D, int WR>
+template <int D, int WR, int RB>
 int stream_grid(int device) {
   static int cached[64] = {0};
   if (device < 0 || device >= 64) device = 0;
@@ -779,7 +879,7 @@ int stream_grid(int device) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_stream_kernel<D, WR>, 256, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_stream_kernel<D, WR, RB>, 256, 0) !=
           hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
@@ -790,19 +890,20 @@ int stream_grid(int device) {
   return g;
 }
 
-template <int D, int WR>
+template <int D, int WR, int RB>
 int32_t launch_stream(AttnArgs a, hipStream_t s) {
+  constexpr int ROWS = 16 * RB * WR;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return IDLM_ERR_HIP;
-  const int grid = stream_grid<D, WR>(dev);
+  const int grid = stream_grid<D, WR, RB>(dev);
   a.nlanes = grid * (4 / WR);
-  hipLaunchKernelGGL((attn_stream_kernel<D, WR>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_stream_kernel<D, WR, RB>), dim3(grid), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
   // Slices only while they fit in one round of resident work-groups (two per
   // CU): otherwise every early-exiting slice costs a round of its own.
-  const int slices = 32 * WR / kMergeRows;
+  const int slices = ROWS / kMergeRows;
   a.mslices = (int64_t)a.B * a.Hkv * slices <= 2 * 256 ? slices : 1;
-  hipLaunchKernelGGL((attn_merge_kernel<D, WR>), dim3(a.B * a.Hkv * a.mslices), dim3(256), 0, s,
+  hipLaunchKernelGGL((attn_merge_kernel<D, ROWS>), dim3(a.B * a.Hkv * a.mslices), dim3(256), 0, s,
                      a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
@@ -843,13 +944,13 @@ int32_t launch_paged_attn(const idlm_isd_dims& d, const Plan& p, const void* q, 
     return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
   }
   if (d.D == 64) {
-    if (ap.WR == 1) return launch_stream<64, 1>(a, s);
-    if (ap.WR == 2) return launch_stream<64, 2>(a, s);
-    return launch_stream<64, 4>(a, s);
+    if (ap.RB == 2) return launch_stream<64, 1, 2>(a, s);
+    if (ap.WR == 1) return launch_stream<64, 1, 4>(a, s);
+    return launch_stream<64, 2, 4>(a, s);
   }
-  if (ap.WR == 1) return launch_stream<128, 1>(a, s);
-  if (ap.WR == 2) return launch_stream<128, 2>(a, s);
-  return launch_stream<128, 4>(a, s);
+  if (ap.RB == 2) return launch_stream<128, 1, 2>(a, s);
+  if (ap.WR == 1) return launch_stream<128, 1, 4>(a, s);
+  return launch_stream<128, 2, 4>(a, s);
 }
 
 }  // namespace idlm

@@ -27,8 +27,9 @@ enum : int32_t { kBadPage = 1, kBadCtx = 2, kBadDraft = 4, kFreeList = 8, kBadLe
 // Attention sizes derived from the dims.
 struct AttnPlan {
   int R, G, RG;   // step rows, heads per KV head, query rows per (b, kv head)
-  int WR;         // waves sharing a run, one per 32 query rows (1, 2 or 4)
-  int RGp;        // RG padded to 32 * WR
+  int RB;         // 16-row MFMA blocks per wave (2 or 4)
+  int WR;         // waves sharing a run (1 or 2)
+  int RGp;        // RG padded to 16 * RB * WR
   int npairs;     // B * Hkv
   int max_lanes;  // wave-lanes the partial-state slots are sized for
 };

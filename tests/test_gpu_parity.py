@@ -88,6 +88,33 @@ def test_small_shapes_full_parity(torch_cuda, case):
     check_accept(w, ds, allow_boundary=0)
 
 
+def scale_k_pages(w, factor):
+    """Multiplies the K block of page i of every sequence by factor(i) (the
+    scores of its tokens scale by the same factor)."""
+    for b in range(w.B):
+        n = (int(w.ctx_lens[b]) + W.PAGE - 1) // W.PAGE
+        for i in range(n):
+            phys = w.page_table[b, i]
+            k = W._store_to_f32(w.kv_pages[phys, 0], w.qkv_dtype) * np.float32(factor(i))
+            w.kv_pages[phys, 0] = W.f32_to_bf16_bits(k)
+
+
+@pytest.mark.parametrize("shape", [(4, 32, 8, 128), (8, 64, 8, 128), (4, 8, 2, 64)],
+                         ids=["n4d128", "n8g8d128", "n4d64"])
+@pytest.mark.parametrize("big", [6.0, 30.0])
+def test_scores_outgrowing_the_first_page(torch_cuda, shape, big):
+    """Every odd page's scores are `big` times larger: a segment that starts on
+    an even page takes a softmax reference far below its later scores
+    (weights up to ~2^35 or ~2^130 against it), so the kernel must detect it
+    and stream the segment again from the true row max."""
+    N, Hq, Hkv, D = shape
+    w = small(f"rising{N}_{D}_{big:g}", B=4, N=N, Hq=Hq, Hkv=Hkv, D=D, V=512,
+              ctx=[2 * N - 1, 40, 700, 2100])
+    scale_k_pages(w, lambda i: big if i % 2 else 1.0)
+    ds = run(w, torch_cuda)
+    check_attn_full(w, ds)
+
+
 @pytest.mark.parametrize("V", [2048 * 1024, 2048 * 1024 - 1])
 def test_largest_vocabulary(torch_cuda, V):
     """The largest vocabulary the acceptance takes (1024 sub-chunks of 2048):
