@@ -18,7 +18,7 @@
  *      resampled from normalize(max(0, p - q)), and the committed prefix is
  *      truncated there ("Introspective Diffusion Language Models", section
  *      "Inference & ISD"; GeekNews summary, section "Inference & ISD").
- *   3. idlm_isd_step: 1 then 2 on one stream.
+ *   3. idlm_isd_step: 1 and 2 side by side (they are independent).
  *   4. idlm_isd_propose: the next step's drafts from this forward's MASK
  *      rows, or a fresh step after a rejection.
  *   5. idlm_isd_gated_lora: R-ISD's adapter on MASK rows after the base
@@ -34,7 +34,11 @@
  *   allocates nothing; per-call scratch lives in the caller's workspace.
  * - Everything is enqueued on `stream` (a hipStream_t passed as void*;
  *   NULL = the default stream) and returns without synchronising, except
- *   idlm_isd_read_status.  The enqueued work is kernel launches only (no
+ *   idlm_isd_read_status.  idlm_isd_step also uses one stream of the
+ *   library's own per device (default priority, non-blocking, made by
+ *   idlm_isd_workspace_init or the first step), forked from `stream` and
+ *   joined back to it with events before the call returns, so work enqueued
+ *   on `stream` afterwards sees the whole step.  The enqueued work is kernel launches only (no
  *   memset or copy nodes, no host synchronisation, no allocation), so every
  *   entry point but idlm_isd_read_status can be captured into a HIP graph
  *   and replayed; scalar arguments (seed, T) are fixed at capture.
@@ -164,8 +168,16 @@ int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const 
                         int32_t* out_accept_len, double* out_debug, void* workspace,
                         size_t ws_bytes, void* stream);
 
-/* One ISD step: idlm_isd_paged_attn then idlm_isd_accept on `stream`.  N
- * must equal d->N (it is repeated to keep the step's own argument list). */
+/* One ISD step: idlm_isd_paged_attn and idlm_isd_accept, which read
+ * different inputs, run side by side: the attention on `stream`, the
+ * acceptance on the library's second stream of this device (forked from
+ * `stream` with an event and joined back to it).  The results equal the
+ * two calls in sequence.  When the second stream cannot be created the two
+ * run in sequence on `stream`.  Steps from several host threads on one
+ * device share that stream (their enqueues are serialised); while one
+ * thread captures a step into a graph, no other thread may run a step on
+ * the same device.  N must equal d->N (it is repeated to keep the step's
+ * own argument list). */
 int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
                       const int32_t* page_table, const int32_t* ctx_lens,
                       const void* logits_clean, const void* logits_mask,

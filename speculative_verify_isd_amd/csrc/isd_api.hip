@@ -4,10 +4,50 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "isd_internal.hpp"
 
 namespace idlm {
 namespace {
+
+// idlm_isd_step runs the acceptance on a second stream of its own, forked
+// from the caller's stream and joined back to it with events: the two stages
+// read different inputs and write disjoint workspace regions (the sticky
+// status word is set with atomic ORs), and run side by side on the chip.
+// One set per device, created once; enqueueing a fork holds the mutex so the
+// event record / wait pairs of concurrent host threads do not interleave.
+struct ForkSet {
+  hipStream_t aux = nullptr;
+  hipEvent_t start = nullptr, done = nullptr;
+  bool ok = false;
+};
+constexpr int kMaxDevices = 64;
+ForkSet g_fork[kMaxDevices];
+std::mutex g_fork_mu;
+
+// The current device's set (created on first use), or nullptr when it cannot
+// be had; the caller holds g_fork_mu.
+ForkSet* fork_set() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ForkSet& f = g_fork[dev];
+  if (f.ok) return &f;
+  if (!f.aux && hipStreamCreateWithFlags(&f.aux, hipStreamNonBlocking) != hipSuccess) {
+    f.aux = nullptr;
+    return nullptr;
+  }
+  if (!f.start && hipEventCreateWithFlags(&f.start, hipEventDisableTiming) != hipSuccess) {
+    f.start = nullptr;
+    return nullptr;
+  }
+  if (!f.done && hipEventCreateWithFlags(&f.done, hipEventDisableTiming) != hipSuccess) {
+    f.done = nullptr;
+    return nullptr;
+  }
+  f.ok = true;
+  return &f;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -137,6 +177,10 @@ int32_t idlm_isd_validate(const idlm_isd_dims* d, float T) {
 int32_t idlm_isd_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
   if (!workspace) return IDLM_ERR_NULL;
   if (((uintptr_t)workspace & 255) != 0) return IDLM_ERR_WORKSPACE;
+  {  // the step's second stream and events, made here outside any capture
+    std::lock_guard<std::mutex> g(g_fork_mu);
+    fork_set();
+  }
   if (ws_bytes == 0) return IDLM_OK;
   return launch_fill_zero(workspace, ws_bytes, (hipStream_t)stream);
 }
@@ -196,10 +240,24 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
   if (!logits_clean || !out_tokens || !out_accept_len) return IDLM_ERR_NULL;
   if (d->N > 1 && (!logits_mask || !draft_tokens)) return IDLM_ERR_NULL;
   hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> g(g_fork_mu);
+  ForkSet* f = fork_set();
+  hipStream_t sa = s;  // the acceptance's stream: the fork, or `stream` itself without one
+  if (f) {
+    if (hipEventRecord(f->start, s) != hipSuccess ||
+        hipStreamWaitEvent(f->aux, f->start, 0) != hipSuccess)
+      return IDLM_ERR_HIP;
+    sa = f->aux;
+  }
   r = launch_paged_attn(*d, p, q, kv_pages, page_table, ctx_lens, attn_out, (char*)workspace, s);
   if (r != IDLM_OK) return r;
-  return launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
-                       out_accept_len, nullptr, (char*)workspace, s);
+  r = launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
+                    out_accept_len, nullptr, (char*)workspace, sa);
+  if (r != IDLM_OK) return r;
+  if (f && (hipEventRecord(f->done, f->aux) != hipSuccess ||
+            hipStreamWaitEvent(s, f->done, 0) != hipSuccess))
+    return IDLM_ERR_HIP;
+  return IDLM_OK;
 }
 
 int32_t idlm_isd_propose(const idlm_isd_dims* d, const void* logits_next,

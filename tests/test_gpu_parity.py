@@ -159,6 +159,27 @@ def test_deterministic_and_reusable_workspace(torch_cuda):
     assert not res["bad"]
 
 
+def test_step_joins_its_second_stream(torch_cuda):
+    """idlm_isd_step runs the acceptance on a stream of its own: work enqueued
+    on the caller's stream right after the step (no synchronisation) must see
+    the step's outputs, equal to the two calls in sequence."""
+    torch = torch_cuda
+    rng = np.random.default_rng(3)
+    ctx = [int(c) for c in rng.integers(256, 4096, size=16, endpoint=True)]
+    w = small("fork", B=16, N=4, Hq=32, Hkv=8, D=128, V=151936, ctx=ctx)
+    ds = run(w, torch)
+    ref = (ds.tokens.clone(), ds.lens.clone(), ds.out.clone())
+    for i in range(4):
+        ds.tokens.fill_(-7)
+        ds.lens.zero_()
+        ds.out.zero_()
+        ds.step()
+        got = (ds.tokens.clone(), ds.lens.clone(), ds.out.clone())  # same stream, no sync
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), f"step {i}"
+        assert torch.equal(got[2].view(torch.int16), ref[2].view(torch.int16)), f"step {i}"
+
+
 def test_device_data_errors_are_flagged(torch_cuda):
     torch = torch_cuda
     from speculative_verify_isd_amd.lib import idlm_isd_read_status, idlm_isd_workspace_init
