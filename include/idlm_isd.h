@@ -172,8 +172,9 @@ int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const 
  * different inputs, run side by side: the attention on `stream`, the
  * acceptance on the library's second stream of this device (forked from
  * `stream` with an event and joined back to it).  The results equal the
- * two calls in sequence.  When the second stream cannot be created the two
- * run in sequence on `stream`.  Steps from several host threads on one
+ * two calls in sequence.  Small steps (B*R*V < 2^23 logits, where the
+ * event hand-over costs more than the overlap saves), or a device where the
+ * second stream cannot be created, run the two in sequence on `stream`.  Steps from several host threads on one
  * device share that stream (their enqueues are serialised); while one
  * thread captures a step into a graph, no other thread may run a step on
  * the same device.  N must equal d->N (it is repeated to keep the step's

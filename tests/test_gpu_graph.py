@@ -1,9 +1,9 @@
 """HIP graph capture of the step.
 
 Every entry point except idlm_isd_read_status records only kernel launches
-on the caller's stream (no memset nodes, no host synchronisation, no
-allocation), so a caller can capture idlm_isd_step into a graph and replay
-it.  Each replay must reproduce the eager outputs bit for bit, also with the
+(no memset nodes, no host synchronisation, no allocation), plus, for a large
+step, an event fork to the library's second stream and the join back, so a
+caller can capture idlm_isd_step into a graph and replay it.  Each replay must reproduce the eager outputs bit for bit, also with the
 program's own eager work (fills, reductions) and synchronisations between
 replays.
 """
@@ -24,14 +24,16 @@ def torch_cuda():
     return torch
 
 
-@pytest.mark.parametrize("T", [1.0, 0.0])
-def test_step_graph_replays_match_eager(torch_cuda, T):
+# V = 151936 makes B * R * V above 2^23, so the captured step forks the
+# acceptance onto the library's second stream; V = 8192 keeps it on one.
+@pytest.mark.parametrize("T,V", [(1.0, 8192), (0.0, 8192), (1.0, 151936)])
+def test_step_graph_replays_match_eager(torch_cuda, T, V):
     torch = torch_cuda
     from speculative_verify_isd_amd.lib import DeviceStep
 
     rng = np.random.default_rng(41)
     ctx = rng.integers(600, 3000, size=8, endpoint=True)
-    w = W.make_workload(f"graph_T{T}", B=8, N=4, Hq=32, Hkv=8, D=128, V=8192, ctx_lens=ctx, T=T,
+    w = W.make_workload(f"graph_T{T}_V{V}", B=8, N=4, Hq=32, Hkv=8, D=128, V=V, ctx_lens=ctx, T=T,
                         seed=5)
     ds = DeviceStep(w)
     ds.step(T=T)
@@ -61,4 +63,4 @@ def test_step_graph_replays_match_eager(torch_cuda, T):
         assert torch.equal(ds.lens, ref[1]), f"replay {i}: lengths"
         assert torch.equal(ds.out.view(torch.int16), ref[2].view(torch.int16)), f"replay {i}: attention"
         assert torch.isfinite(noise)
-    print(f"[graph] T={T}: 4 replays identical to the eager step", flush=True)
+    print(f"[graph] T={T} V={V}: 4 replays identical to the eager step", flush=True)
