@@ -656,6 +656,87 @@ __device__ void merge_slice(const AttnArgs& a, int b, int h, int r0, int npieces
   }
 }
 
+// merge_slice for a pair of at most kSlicePieces pieces: every piece's partial
+// outputs for the slice and its (max, sum) rows are loaded in one round (one
+// (max, sum) per thread), the row maxima, normalisers and scale factors go
+// through LDS, and the pieces are folded in unit order with the same
+// arithmetic as merge_slice.
+constexpr int kSlicePieces = 256 / kMergeRows;
+
+template <int D, int ROWS>
+__device__ void merge_slice_one_round(const AttnArgs& a, int b, int h, int r0, int npieces, int wa,
+                                      int64_t start, int64_t span) {
+  constexpr int D4 = D / 4;
+  constexpr int kSVec = (kMergeRows * D4 + 255) / 256;  // float4 outputs per thread
+  __shared__ float sf_m[kSlicePieces][kMergeRows], sf_l[kSlicePieces][kMergeRows];
+  __shared__ float sf_M[kMergeRows], sf_iL[kMergeRows];
+  const int tid = threadIdx.x;
+  const int nrows = min(kMergeRows, a.RG - r0);
+  const int nvec = nrows * D4;
+  auto slot_of = [&](int k) -> size_t {
+    return (size_t)(wa + k) * 2 + ((k == 0 && start != (int64_t)wa * span) ? 1 : 0);
+  };
+  float4 v[kSlicePieces][kSVec];
+#pragma unroll
+  for (int t = 0; t < kSlicePieces; ++t) {
+    const int k = min(t, npieces - 1);  // clamped, unconditional
+    const float4* po = (const float4*)(a.part_o + (slot_of(k) * ROWS + r0) * D);
+#pragma unroll
+    for (int e = 0; e < kSVec; ++e) v[t][e] = po[min(tid + 256 * e, nvec - 1)];
+  }
+  {
+    const int k = tid / kMergeRows, row = tid % kMergeRows;
+    const float2 ml = a.part_ml[slot_of(min(k, npieces - 1)) * ROWS + r0 + min(row, nrows - 1)];
+    sf_m[k][row] = ml.x;
+    sf_l[k][row] = ml.y;
+  }
+  __syncthreads();
+  if (tid < nrows) {
+    float M = -INFINITY;
+    for (int k = 0; k < npieces; ++k) M = fmaxf(M, sf_m[k][tid]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+    for (int k = 0; k < npieces; ++k) L += sf_l[k][tid] * exp2f(sf_m[k][tid] - Mu);
+    sf_M[tid] = Mu;
+    sf_iL[tid] = 1.f / L;
+  }
+  __syncthreads();
+  {
+    const int k = tid / kMergeRows, row = tid % kMergeRows;
+    sf_l[k][row] = exp2f(sf_m[k][row] - sf_M[row]) * sf_iL[row];  // piece k's scale factor
+  }
+  __syncthreads();
+  float4 O[kSVec];
+#pragma unroll
+  for (int e = 0; e < kSVec; ++e) O[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int t = 0; t < kSlicePieces; ++t)
+    if (t < npieces) {
+#pragma unroll
+      for (int e = 0; e < kSVec; ++e) {
+        const int i = min(tid + 256 * e, nvec - 1);
+        const float f = sf_l[t][i / D4];
+        O[e].x += v[t][e].x * f;
+        O[e].y += v[t][e].y * f;
+        O[e].z += v[t][e].z * f;
+        O[e].w += v[t][e].w * f;
+      }
+    }
+  u16* outp = (u16*)a.out;
+#pragma unroll
+  for (int e = 0; e < kSVec; ++e) {
+    const int i = tid + 256 * e;
+    if (i < nvec) {
+      const int row = r0 + i / D4, d = 4 * (i % D4);
+      const int r = row / a.G, g = row % a.G;
+      const unsigned lo = f32_to_bf16_rne(O[e].x) | ((unsigned)f32_to_bf16_rne(O[e].y) << 16);
+      const unsigned hi = f32_to_bf16_rne(O[e].z) | ((unsigned)f32_to_bf16_rne(O[e].w) << 16);
+      *(uint2*)(outp + (((size_t)b * a.R + r) * a.Hq + (size_t)h * a.G + g) * D + d) =
+          make_uint2(lo, hi);
+    }
+  }
+}
+
 // Combines the pieces of (b, h) pairs that were split across wave-lane runs,
 // in unit order.  a.mslices work-groups per pair: with one, the pair is
 // folded whole, kBatch pieces' loads at a time; with one per slice of
@@ -709,8 +790,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     return (size_t)(wa + k) * 2 + ((k == 0 && start != (int64_t)wa * span) ? 1 : 0);
   };
   if (npieces > kBatch && a.mslices > 1) {
-    if (kMergeRows * slice < a.RG)
-      merge_slice<D, ROWS>(a, b, h, kMergeRows * slice, npieces, wa, start, span);
+    if (kMergeRows * slice < a.RG) {
+      if (npieces <= kSlicePieces)
+        merge_slice_one_round<D, ROWS>(a, b, h, kMergeRows * slice, npieces, wa, start, span);
+      else
+        merge_slice<D, ROWS>(a, b, h, kMergeRows * slice, npieces, wa, start, span);
+    }
     return;
   }
   if (slice != 0) return;

@@ -11,6 +11,9 @@
 #ifndef RING_PAGES_DEFAULT
 #define RING_PAGES_DEFAULT 2
 #endif
+#ifndef MIN_RUN_PAGES_DEFAULT
+#define MIN_RUN_PAGES_DEFAULT 8
+#endif
 
 namespace idlm {
 
@@ -18,7 +21,7 @@ constexpr int kPage = 16;
 constexpr int kSub = 2048;  // acceptance sub-chunk: 256 threads x 8 elements
 constexpr int kMaxSubChunks = 1024;  // V <= kSub * kMaxSubChunks
 constexpr int kMaxWaves = 2048;   // streaming-attention waves resident at once (upper bound)
-constexpr int kMinRunPages = 8;   // shortest run of pages given to one wave-lane
+constexpr int kMinRunPages = MIN_RUN_PAGES_DEFAULT;  // shortest run of pages given to one wave-lane
 constexpr int kRingPages = RING_PAGES_DEFAULT;  // page buffers per attention wave (D = 128)
 
 // Sticky device status bits (workspace word 0).
