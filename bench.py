@@ -1,9 +1,11 @@
 """Benchmark of the ISD verify-and-propose step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c64] [--sigma-index 1]
+                    [--sigma X]
 
-One step = isd_paged_attn over the whole batch (one attention layer) followed
-by isd_accept for the whole batch, on one stream, inputs resident in HBM.
+One step = idlm_isd_step: isd_paged_attn over the whole batch (one attention
+layer) and isd_accept for the whole batch (for large steps beside it, on the
+library's second stream), inputs resident in HBM.
 Default workload: B = 64 sequences (C = 64), N = 4, 32 query / 8 KV heads,
 D = 128, bf16 KV in 16-token pages, contexts ~ U[2048, 16384], vocab 151936,
 logit perturbation sigma = 0.5, T = 1.
@@ -318,6 +320,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c64")
     ap.add_argument("--sigma-index", type=int, default=1)
+    ap.add_argument("--sigma", type=float, default=None,
+                    help="c64 only: this logit perturbation instead of the swept one")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="sequences timed on the oracle (0: the whole batch)")
     ap.add_argument("--cpu-runs", type=int, default=3, help="oracle runs (median)")
@@ -338,7 +342,7 @@ def main():
     from speculative_verify_isd_amd import workloads
     from speculative_verify_isd_amd.lib import DeviceStep
 
-    w = workloads.named_workload(args.workload, args.sigma_index)
+    w = workloads.named_workload(args.workload, args.sigma_index, args.sigma)
     ds = DeviceStep(w)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()

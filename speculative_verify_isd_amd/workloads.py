@@ -227,10 +227,16 @@ def make_workload(name, B, N, Hq, Hkv, D, V, ctx_lens, T, seed, qkv_dtype="bf16"
 
 
 SIGMAS = (0.1, 0.5, 1.5)
+# Perturbations that give a mean sum_v min(p, q) of about 0.97 / 0.9 / 0.6 at
+# T = 1 (the acceptance rates the C = 64 configuration quotes for its sweep,
+# which SIGMAS as written do not reach).
+CALIBRATED_SIGMAS = (0.074, 0.25, 1.07)
 
 
-def named_workload(name, sigma_index=1):
-    """The five named workloads of the module docstring."""
+def named_workload(name, sigma_index=1, sigma=None):
+    """The five named workloads of the module docstring.  For c64, ``sigma``
+    replaces the swept value SIGMAS[sigma_index] (same contexts and seeds;
+    CALIBRATED_SIGMAS give the acceptance rates the configuration names)."""
     if name == "tiny":
         return make_workload("tiny", B=1, N=4, Hq=8, Hkv=2, D=64, V=512, ctx_lens=[256],
                              T=1.0, seed=1000, qkv_dtype="f32", logits_dtype="f32",
@@ -246,8 +252,9 @@ def named_workload(name, sigma_index=1):
                              T=1.0, seed=3000)
     if name == "c64":
         ctx = rng.integers(2048, 16384, size=64, endpoint=True)
-        sigma = SIGMAS[sigma_index]
-        return make_workload(f"c64_s{sigma}", B=64, N=4, Hq=32, Hkv=8, D=128, V=VOCAB,
+        label = "c64_s" if sigma is None else "c64_calibrated_s"
+        sigma = SIGMAS[sigma_index] if sigma is None else float(sigma)
+        return make_workload(f"{label}{sigma}", B=64, N=4, Hq=32, Hkv=8, D=128, V=VOCAB,
                              ctx_lens=ctx, T=1.0, seed=4000 + sigma_index, sigma=sigma,
                              max_pages=16384 // PAGE)
     if name == "c64n8":
