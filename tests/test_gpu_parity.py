@@ -99,8 +99,8 @@ def scale_k_pages(w, factor):
             w.kv_pages[phys, 0] = W.f32_to_bf16_bits(k)
 
 
-@pytest.mark.parametrize("shape", [(4, 32, 8, 128), (8, 64, 8, 128), (4, 8, 2, 64)],
-                         ids=["n4d128", "n8g8d128", "n4d64"])
+@pytest.mark.parametrize("shape", [(4, 32, 8, 128), (4, 64, 8, 128), (8, 64, 8, 128), (4, 8, 2, 64)],
+                         ids=["n4d128", "n4g8d128", "n8g8d128", "n4d64"])
 @pytest.mark.parametrize("big", [6.0, 30.0])
 def test_scores_outgrowing_the_first_page(torch_cuda, shape, big):
     """Every odd page's scores are `big` times larger: a segment that starts on
