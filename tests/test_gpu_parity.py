@@ -235,8 +235,8 @@ def _picks(w, n, seed):
 def test_named_full_size(torch_cuda, name, sig):
     w = W.named_workload(name, sig)
     ds = run(w, torch_cuda)
-    # The extremes and random rows, plus one row of every sequence (so the
-    # tail of the unit list, which is scheduled dynamically, is covered).
+    # The extremes and random rows, plus one row of every sequence (so every
+    # sequence's pairs, and the runs that split them, are sampled).
     rng = np.random.default_rng(11)
     picks = _picks(w, 6, 5) + [(b, int(rng.integers(0, w.R)), int(rng.integers(0, w.Hq)))
                                for b in range(w.B)]
@@ -250,7 +250,8 @@ def test_named_full_size(torch_cuda, name, sig):
 
 # ---------------------------------------------------------------------------
 # a large batch compared element by element: ~90k units over every wave-lane,
-# with pairs split across several lanes (one and two 32-row groups)
+# with pairs split across several lanes (7-row tiles in 32-row waves, 56-row
+# tiles in 64-row waves)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("Hq,D", [(8, 128), (64, 64)])
 def test_large_batch_full(torch_cuda, Hq, D):
