@@ -180,6 +180,53 @@ def test_step_joins_its_second_stream(torch_cuda):
         assert torch.equal(got[2].view(torch.int16), ref[2].view(torch.int16)), f"step {i}"
 
 
+def test_steps_from_two_host_threads(torch_cuda):
+    """Two host threads run forked steps at once, each on its own stream and
+    workspace; both share the library's second stream, and every result must
+    equal the same step run alone."""
+    import threading
+
+    torch = torch_cuda
+    from speculative_verify_isd_amd.lib import DeviceStep
+
+    rng = np.random.default_rng(8)
+    works = [small(f"thread{t}", B=16, N=4, Hq=32, Hkv=8, D=128, V=151936,
+                   ctx=[int(c) for c in rng.integers(256, 3000, size=16, endpoint=True)], seed=40 + t)
+             for t in range(2)]
+    steps = [DeviceStep(w) for w in works]
+    refs = []
+    for ds in steps:
+        ds.attn()
+        ds.accept()
+        torch.cuda.synchronize()
+        refs.append((ds.tokens.clone(), ds.lens.clone(), ds.out.clone()))
+    errors = []
+
+    def worker(t):
+        try:
+            ds, ref = steps[t], refs[t]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for i in range(6):
+                    ds.tokens.fill_(-7)
+                    ds.lens.zero_()
+                    ds.step()
+                    got = (ds.tokens.clone(), ds.lens.clone(), ds.out.clone())
+                    stream.synchronize()
+                    if not (torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+                            and torch.equal(got[2].view(torch.int16), ref[2].view(torch.int16))):
+                        errors.append((t, i))
+        except Exception as e:  # reported below, in the main thread
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+
+
 def test_device_data_errors_are_flagged(torch_cuda):
     torch = torch_cuda
     from speculative_verify_isd_amd.lib import idlm_isd_read_status, idlm_isd_workspace_init
