@@ -816,14 +816,8 @@ int32_t launch_stats(const AccArgs& a, hipStream_t s) {
 }
 
 template <bool VEC, bool F32>
-int32_t launch_all(AccArgs a, int U1, hipStream_t s) {
-  int32_t r;
-  switch (U1) {
-    case 8: r = launch_stats<8, VEC, F32>(a, s); break;
-    case 4: r = launch_stats<4, VEC, F32>(a, s); break;
-    case 2: r = launch_stats<2, VEC, F32>(a, s); break;
-    default: r = launch_stats<1, VEC, F32>(a, s); break;
-  }
+int32_t launch_all(AccArgs a, hipStream_t s) {
+  const int32_t r = launch_stats<kStatsU, VEC, F32>(a, s);
   if (r != IDLM_OK) return r;
   if (a.greedy) {
     // One decision work-group per sequence and no sampling.
@@ -1161,8 +1155,8 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.f32 = d.logits_dtype == IDLM_F32;
   const bool vec = d.V % 8 == 0 && ((uintptr_t)lc % 16) == 0 &&
                    (lm == nullptr || ((uintptr_t)lm % 16) == 0);
-  if (a.f32) return vec ? launch_all<true, true>(a, ap.U1, s) : launch_all<false, true>(a, ap.U1, s);
-  return vec ? launch_all<true, false>(a, ap.U1, s) : launch_all<false, false>(a, ap.U1, s);
+  if (a.f32) return vec ? launch_all<true, true>(a, s) : launch_all<false, true>(a, s);
+  return vec ? launch_all<true, false>(a, s) : launch_all<false, false>(a, s);
 }
 
 }  // namespace idlm

@@ -102,16 +102,7 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   AcceptPlan& c = p->acc;
   c.R = 2 * d.N - 1;
   c.nsub = (int)ceil_div(d.V, kSub);
-  // Stats: the widest per-thread batch (at most 4 vectors: measured faster
-  // than 8 at C = 64) that still gives >= 2048 work-groups.
-  const int64_t rows = (int64_t)std::max(d.B, 1) * c.R;
-  c.U1 = 1;
-  for (int u = 4; u >= 1; u /= 2)
-    if (rows * ceil_div(d.V, (int64_t)kSub * u) >= 2048) {
-      c.U1 = u;
-      break;
-    }
-  c.S1 = (int)ceil_div(d.V, (int64_t)kSub * c.U1);
+  c.S1 = (int)ceil_div(d.V, (int64_t)kSub * kStatsU);
   // ---- workspace layout ----
   size_t o = 0;
   p->off_status = o;

@@ -19,6 +19,12 @@ namespace idlm {
 
 constexpr int kPage = 16;
 constexpr int kSub = 2048;  // acceptance sub-chunk: 256 threads x 8 elements
+// 16-byte vectors per thread in an acceptance stats work-group (a slice of
+// kSub * kStatsU logits).  Measured per acceptance call: C = 64: 4 vectors
+// 26.4 us, 8 vectors 27.7, 2 vectors 34; B = 1: 4 vectors 15.4 us, 2
+// vectors 15.3, 1 vector 17.4 (the decision then merges 75 slices per row
+// instead of 19); B = 16: 23.9 / 25.8 / 32.0 us for 4 / 2 / 1.
+constexpr int kStatsU = 4;
 constexpr int kMaxSubChunks = 1024;  // V <= kSub * kMaxSubChunks
 constexpr int kMaxWaves = 2048;   // streaming-attention waves resident at once (upper bound)
 constexpr int kMinRunPages = MIN_RUN_PAGES_DEFAULT;  // shortest run of pages given to one wave-lane
@@ -41,8 +47,7 @@ struct AttnPlan {
 struct AcceptPlan {
   int R;          // rows per sequence: N clean + K mask
   int nsub;       // kSub-element sub-chunks per row
-  int U1;         // 16-byte vectors per thread in a stats work-group (1, 2, 4 or 8)
-  int S1;         // stats work-groups per row: ceil(V / (kSub * U1))
+  int S1;         // stats work-groups per row: ceil(V / (kSub * kStatsU))
 };
 
 // Per-sequence hand-over from the ratio test to the sampler.
