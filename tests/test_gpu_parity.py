@@ -80,6 +80,13 @@ def test_tiny_named_workload(torch_cuda):
     dict(name="f32_128", B=2, N=4, Hq=16, Hkv=4, D=128, V=777, ctx=[7, 500], qkv="f32",
          logits="f32"),
     dict(name="mha", B=2, N=2, Hq=4, Hkv=4, D=128, V=64, ctx=[3, 260]),
+    # the largest stride: 31 rows and 15 drafts per sequence; a 31-row tile and
+    # a 124-row tile (two 64-row waves per run)
+    dict(name="n16g1", B=3, N=16, Hq=4, Hkv=4, D=128, V=3000, ctx=[31, 500, 1777]),
+    dict(name="n16g4", B=3, N=16, Hq=16, Hkv=4, D=128, V=3000, ctx=[31, 640, 1500]),
+    # many short sequences: most pairs lie whole inside one run
+    dict(name="b400", B=400, N=4, Hq=32, Hkv=8, D=128, V=1000,
+         ctx=[7 + (37 * i) % 190 for i in range(400)]),
 ])
 def test_small_shapes_full_parity(torch_cuda, case):
     w = small(**case)
