@@ -74,7 +74,7 @@ class Cache:
                 self.d_ctx2.cpu().numpy(), int(self.d_count.item()), self.d_stack.cpu().numpy())
 
 
-CASES = [("bf16", 128, 4), ("bf16", 64, 8), ("f32", 64, 4), ("f32", 128, 1)]
+CASES = [("bf16", 128, 4), ("bf16", 64, 8), ("f32", 64, 4), ("f32", 128, 1), ("bf16", 128, 16)]
 
 
 @pytest.mark.parametrize("dtype,D,N", CASES)

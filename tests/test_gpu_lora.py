@@ -33,7 +33,7 @@ def _bits(t):
 
 @pytest.mark.parametrize("B,N,H,O,rank", [
     (4, 4, 256, 200, 32), (64, 4, 4096, 512, 128), (3, 8, 512, 64, 16), (5, 1, 128, 96, 16),
-    (2, 2, 1024, 1000, 256),
+    (2, 2, 1024, 1000, 256), (3, 16, 512, 256, 64),
 ])
 def test_gated_lora_matches_oracle(torch_cuda, B, N, H, O, rank):
     torch = torch_cuda
