@@ -45,7 +45,8 @@ def good(**kw):
 
 def test_validate_accepts_the_step_shapes(so):
     for d in (good(), good(N=8, Hq=64), good(B=1, D=64, Hq=8, Hkv=2, V=512, qkv_dtype="f32",
-                                              logits_dtype="f32"), good(N=1), good(B=0)):
+                                              logits_dtype="f32"), good(N=1), good(B=0),
+              good(N=16, Hq=4, Hkv=4), good(N=16, Hq=16, Hkv=4)):  # 31- and 124-row tiles
         assert L.idlm_isd_validate(d, 1.0) == 0
     assert L.idlm_isd_validate(good(), 0.0) == 0  # greedy
 
