@@ -11,8 +11,9 @@ D = 128, bf16 KV in 16-token pages, contexts ~ U[2048, 16384], vocab 151936,
 logit perturbation sigma = 0.5, T = 1.
 
 Prints one JSON line with steps/s (``value``, from K whole steps between one
-pair of HIP events), committed and accepted-draft tokens/s, per-call times
-(mean, median, p10, p90) of isd_paged_attn and isd_accept from a second
+pair of HIP events), the step-time spread (median, p10, p90 over K more
+steps, one event pair each), committed and accepted-draft tokens/s, per-call
+times (mean, median, p10, p90) of isd_paged_attn and isd_accept from a second
 timed region with events between the two calls (all events on the launch
 stream), the attention roofline against 8 TB/s and the CPU oracle timed on
 the same workload (whole batch, median of 3 single-threaded runs, ~15 s).
@@ -398,6 +399,19 @@ def main():
         torch.cuda.synchronize()
         ms_per_step = float(np.mean([e[0].elapsed_time(e[1]) for e in es]))
     wall = time.perf_counter() - t0
+    if flush:
+        step_t = np.array([e[0].elapsed_time(e[1]) for e in es])
+    else:
+        # Step-time spread: K more back-to-back steps with an event pair
+        # around each (the headline value above has one pair around all K).
+        es = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        torch.cuda.synchronize()
+        for k in range(K):
+            es[k][0].record(stream)
+            ds.step()
+            es[k][1].record(stream)
+        torch.cuda.synchronize()
+        step_t = np.array([e[0].elapsed_time(e[1]) for e in es])
 
     # Timed region 2 (per-kernel): the same K steps as the two calls of the
     # step with events between them, for each call's own duration.
@@ -469,6 +483,8 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_spread": dict(spread(step_t),
+                            steps_per_s_at_median=1000.0 / float(np.median(step_t))),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
