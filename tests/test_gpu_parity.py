@@ -122,6 +122,33 @@ def test_scores_outgrowing_the_first_page(torch_cuda, shape, big):
     check_attn_full(w, ds)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_and_score_scales(torch_cuda, seed):
+    """Seeded random shapes over every attention tiling (32- and 64-row waves,
+    one or two waves per run, D = 64 / 128, N = 1..16), ragged contexts, and
+    for half of the cases K pages scaled by random factors up to 40 (so some
+    segments outgrow their first page's reference and take the re-stream
+    path, in no fixed pattern)."""
+    rng = np.random.default_rng(1000 + seed)
+    while True:
+        N = int(rng.integers(1, 17))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        if (2 * N - 1) * G <= 128:
+            break
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 9))
+    ctx = [int(rng.integers(2 * N - 1, 2500)) for _ in range(B)]
+    w = small(f"rand{seed}", B=B, N=N, Hq=G * Hkv, Hkv=Hkv, D=D, V=int(rng.integers(64, 4000)),
+              ctx=ctx, seed=seed)
+    if seed % 2:
+        f = rng.uniform(0.2, 40.0, size=1 + max(ctx) // 16)
+        scale_k_pages(w, lambda i: float(f[i]))
+    ds = run(w, torch_cuda)
+    check_attn_full(w, ds)
+    check_accept(w, ds, allow_boundary=1)
+
+
 @pytest.mark.parametrize("V", [2048 * 1024, 2048 * 1024 - 1])
 def test_largest_vocabulary(torch_cuda, V):
     """The largest vocabulary the acceptance takes (1024 sub-chunks of 2048):
