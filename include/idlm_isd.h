@@ -38,10 +38,11 @@
  *   library's own per device (default priority, non-blocking, made by
  *   idlm_isd_workspace_init or the first step), forked from `stream` and
  *   joined back to it with events before the call returns, so work enqueued
- *   on `stream` afterwards sees the whole step.  The enqueued work is kernel launches only (no
- *   memset or copy nodes, no host synchronisation, no allocation), so every
- *   entry point but idlm_isd_read_status can be captured into a HIP graph
- *   and replayed; scalar arguments (seed, T) are fixed at capture.
+ *   on `stream` afterwards sees the whole step.  The enqueued work is kernel
+ *   launches only, plus that fork's event records and waits (no memset or
+ *   copy nodes, no host synchronisation, no allocation), so every entry
+ *   point but idlm_isd_read_status can be captured into a HIP graph and
+ *   replayed; scalar arguments (seed, T) are fixed at capture.
  * - A nonzero return is an idlm_status; nothing was enqueued when a call
  *   fails host-side validation.  Host validation needs no GPU.
  * - Bad *device data* (a page id outside [0, num_pages), a context length
@@ -174,11 +175,11 @@ int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const 
  * `stream` with an event and joined back to it).  The results equal the
  * two calls in sequence.  Small steps (B*R*V < 2^23 logits, where the
  * event hand-over costs more than the overlap saves), or a device where the
- * second stream cannot be created, run the two in sequence on `stream`.  Steps from several host threads on one
- * device share that stream (their enqueues are serialised); while one
- * thread captures a step into a graph, no other thread may run a step on
- * the same device.  N must equal d->N (it is repeated to keep the step's
- * own argument list). */
+ * second stream cannot be created, run the two in sequence on `stream`.
+ * Steps from several host threads on one device share that stream (their
+ * enqueues are serialised); while one thread captures a step into a graph,
+ * no other thread may run a step on the same device.  N must equal d->N (it
+ * is repeated to keep the step's own argument list). */
 int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
                       const int32_t* page_table, const int32_t* ctx_lens,
                       const void* logits_clean, const void* logits_mask,

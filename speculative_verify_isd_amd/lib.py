@@ -1,8 +1,10 @@
 """ctypes binding of libidlm_isd.so (C ABI in include/idlm_isd.h).
 
-Argument marshalling only: every function here checks tensor dtypes, devices
-and contiguity, then passes raw device pointers and torch's current HIP
-stream to the entry point of the same name.  No step arithmetic happens in
+Argument marshalling only: every function here checks tensor dtypes,
+contiguity, sizes (each tensor must hold at least the elements the sizes in
+``dims`` imply, since the kernels index by those sizes) and devices, then
+passes raw device pointers and torch's current HIP stream to the entry point
+of the same name.  No step arithmetic happens in
 Python and there is no fallback: if the library is missing, ``load()``
 raises.
 """
@@ -134,19 +136,51 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _ptr(t, dtypes, name, allow_none=False):
+def _ptr(t, dtypes, name, allow_none=False, numel=None):
+    """Device pointer of ``t`` after the checks; ``numel`` is the least
+    number of elements the call will touch."""
     if t is None:
         if allow_none:
             return None
         raise ValueError(f"{name} is required")
     torch = _torch()
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA/HIP tensor")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; these sizes need {numel}")
+    if not _on_device(t):
+        raise TypeError(f"{name} must be a CUDA/HIP tensor")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _on_device(t):
+    return t.is_cuda
+
+
+def _sizes(dims):
+    """Element counts of the step's arrays for ``dims`` (idlm_isd.h layouts);
+    all zero for B = 0, a call that reads and writes nothing."""
+    B, N, V = dims.B, dims.N, dims.V
+    R, K = 2 * N - 1, N - 1
+    on = 1 if B > 0 else 0
+    return {
+        "q": B * R * dims.Hq * dims.D,
+        "kv": on * dims.num_pages * 2 * dims.Hkv * 16 * dims.D,
+        "kv_new": B * R * dims.Hkv * dims.D,
+        "page_table": B * dims.max_pages,
+        "B": B,
+        "clean": B * N * V,
+        "mask": B * K * V,
+        "drafts": B * K,
+        "tokens": B * N,
+        "debug": B * (N + 1) * 4,
+        "pool": on * dims.num_pages,
+        "one": on,
+    }
 
 
 def _fdt(dims_code):
@@ -186,24 +220,29 @@ def idlm_isd_workspace_init(ws):
 
 def idlm_isd_paged_attn(dims, q, kv_pages, page_table, ctx_lens, attn_out, ws):
     ft = _fdt(dims.qkv_dtype)
+    n = _sizes(dims)
     _check(load().idlm_isd_paged_attn(
-        ctypes.byref(dims), _ptr(q, ft, "q"), _ptr(kv_pages, ft, "kv_pages"),
-        _ptr(page_table, _i32(), "page_table"), _ptr(ctx_lens, _i32(), "ctx_lens"),
-        _ptr(attn_out, ft, "attn_out"), _ptr(ws, (_torch().uint8,), "workspace"), ws.numel(),
-        _stream()), "idlm_isd_paged_attn")
+        ctypes.byref(dims), _ptr(q, ft, "q", numel=n["q"]),
+        _ptr(kv_pages, ft, "kv_pages", numel=n["kv"]),
+        _ptr(page_table, _i32(), "page_table", numel=n["page_table"]),
+        _ptr(ctx_lens, _i32(), "ctx_lens", numel=n["B"]),
+        _ptr(attn_out, ft, "attn_out", numel=n["q"]), _ptr(ws, (_torch().uint8,), "workspace"),
+        ws.numel(), _stream()), "idlm_isd_paged_attn")
 
 
 def idlm_isd_accept(dims, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
                     out_accept_len, out_debug, ws):
     ft = _fdt(dims.logits_dtype)
     torch = _torch()
+    n = _sizes(dims)
     _check(load().idlm_isd_accept(
-        ctypes.byref(dims), _ptr(logits_clean, ft, "logits_clean"),
-        _ptr(logits_mask, ft, "logits_mask", allow_none=True),
-        _ptr(draft_tokens, _i32(), "draft_tokens", allow_none=True),
+        ctypes.byref(dims), _ptr(logits_clean, ft, "logits_clean", numel=n["clean"]),
+        _ptr(logits_mask, ft, "logits_mask", allow_none=True, numel=n["mask"]),
+        _ptr(draft_tokens, _i32(), "draft_tokens", allow_none=True, numel=n["drafts"]),
         ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), float(T),
-        _ptr(out_tokens, _i32(), "out_tokens"), _ptr(out_accept_len, _i32(), "out_accept_len"),
-        _ptr(out_debug, (torch.float64,), "out_debug", allow_none=True),
+        _ptr(out_tokens, _i32(), "out_tokens", numel=n["tokens"]),
+        _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
+        _ptr(out_debug, (torch.float64,), "out_debug", allow_none=True, numel=n["debug"]),
         _ptr(ws, (torch.uint8,), "workspace"), ws.numel(), _stream()), "idlm_isd_accept")
 
 
@@ -212,24 +251,32 @@ def idlm_isd_step(dims, q, kv_pages, page_table, ctx_lens, logits_clean, logits_
     fq = _fdt(dims.qkv_dtype)
     fl = _fdt(dims.logits_dtype)
     torch = _torch()
+    n = _sizes(dims)
     _check(load().idlm_isd_step(
-        ctypes.byref(dims), _ptr(q, fq, "q"), _ptr(kv_pages, fq, "kv_pages"),
-        _ptr(page_table, _i32(), "page_table"), _ptr(ctx_lens, _i32(), "ctx_lens"),
-        _ptr(logits_clean, fl, "logits_clean"),
-        _ptr(logits_mask, fl, "logits_mask", allow_none=True),
-        _ptr(draft_tokens, _i32(), "draft_tokens", allow_none=True),
+        ctypes.byref(dims), _ptr(q, fq, "q", numel=n["q"]),
+        _ptr(kv_pages, fq, "kv_pages", numel=n["kv"]),
+        _ptr(page_table, _i32(), "page_table", numel=n["page_table"]),
+        _ptr(ctx_lens, _i32(), "ctx_lens", numel=n["B"]),
+        _ptr(logits_clean, fl, "logits_clean", numel=n["clean"]),
+        _ptr(logits_mask, fl, "logits_mask", allow_none=True, numel=n["mask"]),
+        _ptr(draft_tokens, _i32(), "draft_tokens", allow_none=True, numel=n["drafts"]),
         ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), int(N), float(T),
-        _ptr(out_tokens, _i32(), "out_tokens"), _ptr(out_accept_len, _i32(), "out_accept_len"),
-        _ptr(attn_out, fq, "attn_out"), _ptr(ws, (torch.uint8,), "workspace"), ws.numel(),
-        _stream()), "idlm_isd_step")
+        _ptr(out_tokens, _i32(), "out_tokens", numel=n["tokens"]),
+        _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
+        _ptr(attn_out, fq, "attn_out", numel=n["q"]), _ptr(ws, (torch.uint8,), "workspace"),
+        ws.numel(), _stream()), "idlm_isd_step")
 
 
 def idlm_isd_propose(dims, logits_next, draft_tokens, accept_len, seed, T, next_drafts, ws):
+    n = _sizes(dims)
     _check(load().idlm_isd_propose(
-        ctypes.byref(dims), _ptr(logits_next, _fdt(dims.logits_dtype), "logits_next"),
-        _ptr(draft_tokens, _i32(), "draft_tokens"), _ptr(accept_len, _i32(), "accept_len"),
+        ctypes.byref(dims),
+        _ptr(logits_next, _fdt(dims.logits_dtype), "logits_next", numel=n["mask"]),
+        _ptr(draft_tokens, _i32(), "draft_tokens", numel=n["drafts"]),
+        _ptr(accept_len, _i32(), "accept_len", numel=n["B"] if dims.N > 1 else 0),  # N = 1: no-op
         ctypes.c_uint64(int(seed) & (2**64 - 1)), ctypes.c_float(float(T)),
-        _ptr(next_drafts, _i32(), "next_drafts"), _ptr(ws, (_torch().uint8,), "workspace"),
+        _ptr(next_drafts, _i32(), "next_drafts", numel=n["drafts"]),
+        _ptr(ws, (_torch().uint8,), "workspace"),
         ctypes.c_size_t(ws.numel()), _stream()),
         "idlm_isd_propose")
 
@@ -251,10 +298,14 @@ def alloc_lora_workspace(ldims, device="cuda"):
 def idlm_isd_gated_lora(ldims, y_base, x, lora_a, lora_b, scale, y_out, ws):
     torch = _torch()
     bf = (torch.bfloat16,)
+    M = ldims.B * (2 * ldims.N - 1)
+    w = 1 if M > 0 else 0  # B = 0 reads no weights
     _check(load().idlm_isd_gated_lora(
-        ctypes.byref(ldims), _ptr(y_base, (torch.float32,), "y_base"), _ptr(x, bf, "x"),
-        _ptr(lora_a, bf, "lora_a"), _ptr(lora_b, bf, "lora_b"), ctypes.c_float(float(scale)),
-        _ptr(y_out, bf, "y_out"), _ptr(ws, (torch.uint8,), "workspace"),
+        ctypes.byref(ldims), _ptr(y_base, (torch.float32,), "y_base", numel=M * ldims.O),
+        _ptr(x, bf, "x", numel=M * ldims.H),
+        _ptr(lora_a, bf, "lora_a", numel=w * ldims.rank * ldims.H),
+        _ptr(lora_b, bf, "lora_b", numel=w * ldims.O * ldims.rank), ctypes.c_float(float(scale)),
+        _ptr(y_out, bf, "y_out", numel=M * ldims.O), _ptr(ws, (torch.uint8,), "workspace"),
         ctypes.c_size_t(ws.numel()), _stream()),
         "idlm_isd_gated_lora")
 
@@ -262,22 +313,31 @@ def idlm_isd_gated_lora(ldims, y_base, x, lora_a, lora_b, scale, y_out, ws):
 def idlm_isd_kv_append(dims, k_new, v_new, ctx_before, ctx_after, kv_pages, page_table,
                        free_pages, free_count, ws):
     dt = _fdt(dims.qkv_dtype)
+    n = _sizes(dims)
     _check(load().idlm_isd_kv_append(
-        ctypes.byref(dims), _ptr(k_new, dt, "k_new"), _ptr(v_new, dt, "v_new"),
-        _ptr(ctx_before, _i32(), "ctx_before"), _ptr(ctx_after, _i32(), "ctx_after"),
-        _ptr(kv_pages, dt, "kv_pages"), _ptr(page_table, _i32(), "page_table"),
-        _ptr(free_pages, _i32(), "free_pages"), _ptr(free_count, _i32(), "free_count"),
+        ctypes.byref(dims), _ptr(k_new, dt, "k_new", numel=n["kv_new"]),
+        _ptr(v_new, dt, "v_new", numel=n["kv_new"]),
+        _ptr(ctx_before, _i32(), "ctx_before", numel=n["B"]),
+        _ptr(ctx_after, _i32(), "ctx_after", numel=n["B"]),
+        _ptr(kv_pages, dt, "kv_pages", numel=n["kv"]),
+        _ptr(page_table, _i32(), "page_table", numel=n["page_table"]),
+        _ptr(free_pages, _i32(), "free_pages", numel=n["pool"]),
+        _ptr(free_count, _i32(), "free_count", numel=n["one"]),
         _ptr(ws, (_torch().uint8,), "workspace"), ctypes.c_size_t(ws.numel()), _stream()),
         "idlm_isd_kv_append")
 
 
 def idlm_isd_kv_rollback(dims, ctx_lens, accept_len, ctx_after, page_table, free_pages,
                          free_count, ws):
+    n = _sizes(dims)
     _check(load().idlm_isd_kv_rollback(
-        ctypes.byref(dims), _ptr(ctx_lens, _i32(), "ctx_lens"),
-        _ptr(accept_len, _i32(), "accept_len"), _ptr(ctx_after, _i32(), "ctx_after"),
-        _ptr(page_table, _i32(), "page_table"), _ptr(free_pages, _i32(), "free_pages"),
-        _ptr(free_count, _i32(), "free_count"), _ptr(ws, (_torch().uint8,), "workspace"),
+        ctypes.byref(dims), _ptr(ctx_lens, _i32(), "ctx_lens", numel=n["B"]),
+        _ptr(accept_len, _i32(), "accept_len", numel=n["B"]),
+        _ptr(ctx_after, _i32(), "ctx_after", numel=n["B"]),
+        _ptr(page_table, _i32(), "page_table", numel=n["page_table"]),
+        _ptr(free_pages, _i32(), "free_pages", numel=n["pool"]),
+        _ptr(free_count, _i32(), "free_count", numel=n["one"]),
+        _ptr(ws, (_torch().uint8,), "workspace"),
         ctypes.c_size_t(ws.numel()), _stream()),
         "idlm_isd_kv_rollback")
 

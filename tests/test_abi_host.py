@@ -160,3 +160,104 @@ def test_gated_lora_validates_before_launch(so):
                                   fake, ctypes.c_float(1.0), fake, fake, n, None) == 3
     assert so.idlm_isd_gated_lora(ctypes.byref(ok), fake, fake, fake, fake,
                                   ctypes.c_float(float("nan")), fake, fake, n, None) == 2
+
+
+# ---------------------------------------------------------------------------
+# The Python binding's checks, on CPU tensors: the device check is stubbed to
+# pass and the stream lookup (the last argument of every call) to raise, so
+# every check runs and no call reaches the library.
+# ---------------------------------------------------------------------------
+class _Reached(Exception):
+    pass
+
+
+@pytest.fixture
+def host_binding(so, monkeypatch):
+    def stream():
+        raise _Reached()
+
+    monkeypatch.setattr(L, "_on_device", lambda t: True)
+    monkeypatch.setattr(L, "_stream", stream)
+    return L
+
+def _binding_args():
+    import torch
+
+    B, N, Hq, Hkv, D, V, mp, P = 2, 4, 8, 2, 64, 100, 4, 8
+    R, K = 2 * N - 1, N - 1
+    d = L.make_dims(B, N, Hq, Hkv, D, V, mp, P)
+    bf, i32 = torch.bfloat16, torch.int32
+    t = {
+        "q": torch.zeros(B * R * Hq * D, dtype=bf),
+        "kv_pages": torch.zeros(P * 2 * Hkv * 16 * D, dtype=bf),
+        "page_table": torch.zeros(B * mp, dtype=i32),
+        "ctx_lens": torch.zeros(B, dtype=i32),
+        "attn_out": torch.zeros(B * R * Hq * D, dtype=bf),
+        "logits_clean": torch.zeros(B * N * V, dtype=bf),
+        "logits_mask": torch.zeros(B * K * V, dtype=bf),
+        "draft_tokens": torch.zeros(B * K, dtype=i32),
+        "out_tokens": torch.zeros(B * N, dtype=i32),
+        "out_accept_len": torch.zeros(B, dtype=i32),
+        "workspace": torch.zeros(L.idlm_isd_workspace_bytes(d), dtype=torch.uint8),
+    }
+    return d, t
+
+
+def _call_step(d, t):
+    L.idlm_isd_step(d, t["q"], t["kv_pages"], t["page_table"], t["ctx_lens"], t["logits_clean"],
+                    t["logits_mask"], t["draft_tokens"], 1, d.N, 1.0, t["out_tokens"],
+                    t["out_accept_len"], t["attn_out"], t["workspace"])
+
+
+def test_binding_names_a_short_tensor(host_binding):
+    d, t = _binding_args()
+    for name in ("q", "kv_pages", "page_table", "ctx_lens", "attn_out", "logits_clean",
+                 "logits_mask", "draft_tokens", "out_tokens", "out_accept_len"):
+        short = dict(t)
+        short[name] = t[name][:-1]
+        with pytest.raises(ValueError, match=name):
+            _call_step(d, short)
+    with pytest.raises(_Reached):  # every size right
+        _call_step(d, t)
+    with pytest.raises(ValueError, match="logits_mask"):  # N = 4 needs MASK rows
+        _call_step(d, dict(t, logits_mask=t["logits_mask"][:0]))
+    # B = 0 is a no-op: empty tensors pass
+    d0 = L.make_dims(0, 4, 8, 2, 64, 100, 4, 8)
+    with pytest.raises(_Reached):
+        _call_step(d0, {k: (v if k == "workspace" else v[:0]) for k, v in t.items()})
+
+
+def test_binding_checks_every_entry_points_sizes(host_binding):
+    import torch
+
+    d, t = _binding_args()
+    with pytest.raises(ValueError, match="logits_next"):
+        L.idlm_isd_propose(d, t["logits_mask"][:-1], t["draft_tokens"], t["out_accept_len"], 1,
+                           1.0, t["draft_tokens"], t["workspace"])
+    d1 = L.make_dims(2, 1, 8, 2, 64, 100, 4, 8)  # N = 1: a no-op that reads nothing
+    with pytest.raises(_Reached):
+        L.idlm_isd_propose(d1, t["q"][:0], t["ctx_lens"][:0], t["ctx_lens"][:0], 1, 1.0,
+                           t["ctx_lens"][:0], t["workspace"])
+    i32 = torch.int32
+    with pytest.raises(ValueError, match="free_pages"):
+        L.idlm_isd_kv_append(d, t["q"][:2 * 7 * 2 * 64], t["q"][:2 * 7 * 2 * 64], t["ctx_lens"],
+                             t["ctx_lens"], t["kv_pages"], t["page_table"],
+                             torch.zeros(d.num_pages - 1, dtype=i32), torch.zeros(1, dtype=i32),
+                             t["workspace"])
+    with pytest.raises(ValueError, match="k_new"):
+        L.idlm_isd_kv_append(d, t["q"][:10], t["q"][:2 * 7 * 2 * 64], t["ctx_lens"],
+                             t["ctx_lens"], t["kv_pages"], t["page_table"],
+                             torch.zeros(d.num_pages, dtype=i32), torch.zeros(1, dtype=i32),
+                             t["workspace"])
+    with pytest.raises(ValueError, match="free_count"):
+        L.idlm_isd_kv_rollback(d, t["ctx_lens"], t["out_accept_len"], t["ctx_lens"],
+                               t["page_table"], torch.zeros(d.num_pages, dtype=i32),
+                               torch.zeros(0, dtype=i32), t["workspace"])
+    ld = L.LoraDims(2, 4, 64, 32, 16)
+    M = 2 * 7
+    bf = torch.bfloat16
+    with pytest.raises(ValueError, match="lora_b"):
+        L.idlm_isd_gated_lora(ld, torch.zeros(M * 32), torch.zeros(M * 64, dtype=bf),
+                              torch.zeros(16 * 64, dtype=bf), torch.zeros(32 * 16 - 1, dtype=bf),
+                              0.5, torch.zeros(M * 32, dtype=bf),
+                              torch.zeros(64, dtype=torch.uint8))
