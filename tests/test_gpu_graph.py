@@ -3,9 +3,9 @@
 Every entry point except idlm_isd_read_status records only kernel launches
 (no memset nodes, no host synchronisation, no allocation), plus, for a large
 step, an event fork to the library's second stream and the join back, so a
-caller can capture idlm_isd_step into a graph and replay it.  Each replay must reproduce the eager outputs bit for bit, also with the
-program's own eager work (fills, reductions) and synchronisations between
-replays.
+caller can capture idlm_isd_step into a graph and replay it.  Each replay
+must reproduce the eager outputs bit for bit, also with the program's own
+eager work (fills, reductions) and synchronisations between replays.
 """
 
 import numpy as np
