@@ -87,6 +87,10 @@ def test_tiny_named_workload(torch_cuda):
     # many short sequences: most pairs lie whole inside one run
     dict(name="b400", B=400, N=4, Hq=32, Hkv=8, D=128, V=1000,
          ctx=[7 + (37 * i) % 190 for i in range(400)]),
+    # the largest tile, R * G = 128 (one KV head for 128 query heads), no padding rows
+    dict(name="g128", B=2, N=1, Hq=128, Hkv=1, D=64, V=50, ctx=[1, 300]),
+    # a one-token vocabulary: p = q = 1, every draft kept, the bonus token is 0
+    dict(name="v1", B=3, N=4, Hq=8, Hkv=2, D=64, V=1, ctx=[7, 20, 100]),
 ])
 def test_small_shapes_full_parity(torch_cuda, case):
     w = small(**case)
