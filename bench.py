@@ -79,13 +79,13 @@ def attn_flops(w):
 
 def _profile_record(w):
     """The committed rocprofv3 summary of the attention (HBM counters and MFMA
-    counters) at C = 64, N = 4, or None for another workload or when
+    counters) for this workload (every sigma of C = 64, N = 4 shares one: the
+    attention does not depend on it), or None when there is none or when
     isd_attn.hip changed after the counters were taken."""
     import hashlib
 
-    if not w.name.startswith("c64_s"):
-        return None
-    tfile = os.path.join(ROOT, "profiles", "isd_paged_attn_c64_traffic.json")
+    tag = "c64" if w.name.startswith("c64_s") else w.name
+    tfile = os.path.join(ROOT, "profiles", f"isd_paged_attn_{tag}_traffic.json")
     if not os.path.exists(tfile):
         return None
     t = json.load(open(tfile))
