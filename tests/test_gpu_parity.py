@@ -79,6 +79,8 @@ def test_tiny_named_workload(torch_cuda):
     dict(name="n1", B=4, N=1, Hq=32, Hkv=8, D=128, V=5000, ctx=[1, 2, 16, 700]),    # plain decode
     dict(name="f32_128", B=2, N=4, Hq=16, Hkv=4, D=128, V=777, ctx=[7, 500], qkv="f32",
          logits="f32"),
+    dict(name="f32_g120", B=2, N=8, Hq=64, Hkv=8, D=64, V=300, ctx=[15, 400], qkv="f32",
+         logits="f32"),                                                             # 120 rows
     dict(name="mha", B=2, N=2, Hq=4, Hkv=4, D=128, V=64, ctx=[3, 260]),
     # the largest stride: 31 rows and 15 drafts per sequence; a 31-row tile and
     # a 124-row tile (two 64-row waves per run)
