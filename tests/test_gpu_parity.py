@@ -155,6 +155,16 @@ def test_random_shapes_and_score_scales(torch_cuda, seed):
     check_accept(w, ds, allow_boundary=1)
 
 
+@pytest.mark.parametrize("T", [0.05, 0.3, 2.5, 20.0])
+def test_temperatures(torch_cuda, T):
+    """Low T makes p and q nearly one-hot: most weights underflow and the
+    residual sums of max(0, p - q) get tiny (down to ~1e-83 at T = 0.05 on
+    these rows).  High T makes them nearly uniform."""
+    w = small(f"temp{T}", B=16, N=4, Hq=8, Hkv=2, D=64, V=5000, ctx=[20] * 16, T=T, seed=11)
+    ds = run(w, torch_cuda)
+    check_accept(w, ds, allow_boundary=1)
+
+
 @pytest.mark.parametrize("V", [2048 * 1024, 2048 * 1024 - 1])
 def test_largest_vocabulary(torch_cuda, V):
     """The largest vocabulary the acceptance takes (1024 sub-chunks of 2048):
