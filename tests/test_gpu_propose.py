@@ -84,6 +84,8 @@ def run_case(torch, B, N, V, dtype, T, seed, keep_frac=0.6):
     (16, 4, 151936, "bf16", 1.0), (64, 4, 151936, "bf16", 0.7), (8, 8, 151936, "bf16", 1.0),
     (16, 4, 151936, "bf16", 0.0), (12, 4, 512, "f32", 1.0), (12, 3, 1000, "f32", 1.0),
     (5, 4, 77, "bf16", 1.0), (3, 16, 5000, "bf16", 1.0),
+    # nearly one-hot (most weights underflow) and nearly uniform proposals
+    (16, 4, 5000, "bf16", 0.05), (16, 4, 5000, "bf16", 20.0),
 ])
 def test_propose_matches_oracle(torch_cuda, B, N, V, dtype, T):
     run_case(torch_cuda, B, N, V, dtype, T, seed=B * 131 + N)
