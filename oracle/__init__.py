@@ -29,6 +29,9 @@ tpf        The tokens-per-forward closed form and the two-state decode chain
            it is the stationary mean of.
 kv_cache   KV-cache append (before attention) and rollback to the accepted
            prefix (after acceptance), with a free-list page stack.
+propose    The next step's drafts from this forward's MASK rows, and the
+           fresh / verify alternation.
+lora       R-ISD's gated LoRA on MASK rows after the base projection.
 dtypes     Exact widening of bfloat16 bit patterns.
 
 Every function listed has at least one pin in ``tests/`` that ties it to
