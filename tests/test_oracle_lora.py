@@ -9,9 +9,8 @@ from oracle.lora import f64_to_bf16_rne, gated_lora
 def _nearest_bf16(v):
     """Exhaustive nearest bfloat16 (ties to the even pattern) of finite v."""
     pats = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    pats = pats[((pats >> 7) & 0xFF) != 0xFF]  # finite patterns (exponent not all ones)
     vals = bf16_bits_to_f64(pats)
-    ok = np.isfinite(vals)
-    pats, vals = pats[ok], vals[ok]
     d = np.abs(vals - v)
     best = d.min()
     cands = pats[d == best]
