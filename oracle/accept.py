@@ -28,8 +28,10 @@ Readings taken where the pages are silent
 * Residual.  At the first rejected position j the committed token is drawn
   from normalize(max(0, p_j - q_j)), the only rule under which the output
   follows p; if that residual sums to zero, p_j is used.
-* Comparison.  Draft i is kept iff p_i(x) >= q_i(x) or u_i * q_i(x) < p_i(x),
-  which is a draw with probability min(1, p/q) without a division.
+* Comparison.  Draft i is kept iff p_i(x) > 0 and (p_i(x) >= q_i(x) or
+  u_i * q_i(x) < p_i(x)), which is a draw with probability min(1, p/q)
+  without a division; a token p gives no mass is never kept (min(1, 0/q) is
+  0, and with q(x) = 0 as well such a draft could not have been proposed).
 * Inverse CDF.  t = u' * sum(w); the token is the smallest v (ascending
   vocabulary order) whose running sum of w exceeds t; if rounding leaves
   none, the largest v with positive weight.
@@ -102,7 +104,8 @@ def accept_with_uniforms(P, Q, drafts, u, u2):
     u      K ratio-test uniforms (u[i] used for draft i)
     u2     K+1 sampling uniforms (u2[j] used at the resample/bonus index j)
 
-    Returns (accept_len, tokens[N] padded with -1, info dict).
+    Returns (accept_len, tokens[N] padded with -1, info dict); info["w"] is
+    the weight row the token was drawn from (unnormalised).
     """
     N = len(P)
     K = N - 1
@@ -117,7 +120,7 @@ def accept_with_uniforms(P, Q, drafts, u, u2):
         info["q"].append(q)
         info["u"].append(float(u[i]))
         info["u2"].append(float(u2[i]))
-        if not (p >= q or u[i] * q < p):
+        if not (p > 0 and (p >= q or u[i] * q < p)):
             j = i
             break
     if j < kp:
@@ -133,7 +136,7 @@ def accept_with_uniforms(P, Q, drafts, u, u2):
     t = float(u2[j]) * total
     v, lo, hi = inverse_cdf(w, t)
     tokens = [int(x) for x in drafts[:j]] + [v] + [-1] * (N - j - 1)
-    info.update(j=j, total=total, t=t, cdf_lo=lo, cdf_hi=hi, u2_used=float(u2[j]))
+    info.update(j=j, total=total, t=t, cdf_lo=lo, cdf_hi=hi, u2_used=float(u2[j]), w=w)
     return j + 1, tokens, info
 
 

@@ -2,8 +2,9 @@
 compare the library's outputs with it.
 
 Tolerances (the oracle is float64; the library computes attention with bf16
-MFMA and float32 softmax/accumulation, acceptance with float32 exponentials
-and float64 sums):
+MFMA and float32 softmax/accumulation; the acceptance's row statistics with
+float32 exponentials summed in float64, its sampling weights wholly in
+float64):
 
 * attention: normwise per head vector, max|gpu - ref| / max|ref| over d,
   at most 2e-2 for bf16 storage and 1e-4 for float32 storage;
@@ -11,7 +12,11 @@ and float64 sums):
 * accept lengths and committed tokens: equal, except at boundary decisions,
   which are counted and reported: a ratio test with |u - p/q| < 1e-6 (or
   |p - q| < 1e-6 q), or an inverse-CDF pick whose threshold t lies within
-  1e-8 * sum(w) of a cumulative-sum boundary.
+  1e-12 * sum(w) of a cumulative-sum boundary (float64 weights on both
+  sides).
+
+The library takes T as float32, so the oracle is evaluated at that same
+value (float(np.float32(T))).
 """
 
 import numpy as np
@@ -23,7 +28,7 @@ from oracle.dtypes import to_f64
 ATTN_TOL = {"bf16": 2e-2, "f32": 1e-4}
 PROB_TOL = 1e-5
 RATIO_BAND = 1e-6
-CDF_BAND = 1e-8
+CDF_BAND = 1e-12
 
 
 def q_f64(w):
@@ -46,9 +51,14 @@ def normwise_err(got, ref):
     return float((num / den).max())
 
 
+def t32(T):
+    """The temperature as the library receives it (a float32)."""
+    return float(np.float32(T))
+
+
 def oracle_accept(w, seed=None, T=None):
     return oracle_accept_batch(w.logits_clean, w.logits_mask, w.draft_tokens,
-                               w.seed if seed is None else seed, w.T if T is None else T,
+                               w.seed if seed is None else seed, t32(w.T if T is None else T),
                                dtype=w.logits_dtype)
 
 

@@ -269,3 +269,37 @@ def test_temperature_scales_logits():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     for ia, ib in zip(a[2], b[2]):
         assert np.allclose(ia["p"], ib["p"], rtol=1e-12) and np.allclose(ia["q"], ib["q"], rtol=1e-12)
+
+
+def test_draft_without_mass_under_p_is_rejected():
+    """min(1, p(x)/q(x)) is 0 when p(x) = 0: such a draft is never kept, even
+    when q(x) = 0 too (a draft no proposal could have made).  Greedy (T = 0):
+    a draft that is the argmax of neither its clean nor its MASK row is
+    rejected and the clean argmax is committed in its place.  Sampled: a
+    draft whose logit is -1000 below both rows' maxima has p(x) = q(x) = 0
+    exactly in float64 and is rejected for every u."""
+    rng = np.random.default_rng(14)
+    V, N, B = 20, 4, 60
+    lc = rng.standard_normal((B, N, V)).astype(np.float32)
+    lm = rng.standard_normal((B, N - 1, V)).astype(np.float32)
+    am_c, am_m = lc.argmax(-1), lm.argmax(-1)
+    drafts = np.empty((B, N - 1), dtype=np.int32)
+    for b in range(B):
+        for i in range(N - 1):
+            drafts[b, i] = next(v for v in range(V) if v != am_c[b, i] and v != am_m[b, i])
+    toks, lens, _ = isd_accept(lc, lm, drafts, 7, 0.0, dtype="f32")
+    assert np.all(lens == 1)
+    assert np.array_equal(toks[:, 0], am_c[:, 0])
+
+    lc2, lm2 = lc.astype(np.float64), lm.astype(np.float64)
+    x = 5
+    lc2[:, 0, x] = -1000.0
+    lm2[:, 0, x] = -1000.0
+    d2 = np.full((B, N - 1), x, dtype=np.int32)
+    _, lens2, infos = isd_accept(lc2, lm2, d2, 8, 1.0)
+    assert all(info["p"][0] == 0.0 and info["q"][0] == 0.0 for info in infos)
+    assert np.all(lens2 == 1)
+    P = [softmax_t(r, 1.0) for r in lc2[0]]
+    Q = [softmax_t(r, 1.0) for r in lm2[0]]
+    for u in (0.0, 0.5, TOP):
+        assert not _accepted_at(P, Q, list(d2[0]), 0, u)
