@@ -55,6 +55,10 @@
  *   per concurrent stream.  The kernels use no atomic counters: launch
  *   boundaries order every hand-over, so results do not depend on
  *   scheduling.
+ * - Workspace: the first idlm_isd_workspace_state_bytes(d) bytes are state
+ *   kept between calls (the sticky status word); idlm_isd_workspace_init
+ *   zeroes them.  The rest is scratch that every call writes before it
+ *   reads, so its contents between calls do not matter.
  *
  * Symbols: B batch, N stride, R = 2N-1 query rows, K = N-1 drafts, Hq / Hkv
  * query / KV heads, G = Hq/Hkv, D head dim, V vocabulary, P pool pages.
@@ -114,9 +118,14 @@ typedef struct {
  * invalid sizes.  Host only. */
 size_t idlm_isd_workspace_bytes(const idlm_isd_dims* d);
 
+/* Leading bytes of that workspace holding state kept between calls (see
+ * the conventions above); 0 for invalid sizes.  Host only. */
+size_t idlm_isd_workspace_state_bytes(const idlm_isd_dims* d);
+
 /* Check sizes and temperature without touching the GPU.  Returns IDLM_OK,
- * IDLM_ERR_NULL, IDLM_ERR_DIMS, IDLM_ERR_UNSUPPORTED or
- * IDLM_ERR_TEMPERATURE.  Host only. */
+ * IDLM_ERR_NULL, IDLM_ERR_DIMS, IDLM_ERR_UNSUPPORTED (also for sizes whose
+ * grids would not fit one dispatch: more than 2^32 - 1 work-items) or
+ * IDLM_ERR_TEMPERATURE (T < 0, not finite, or 0 < T < 2^-126).  Host only. */
 int32_t idlm_isd_validate(const idlm_isd_dims* d, float T);
 
 /* Prepare a workspace for first use: zeroes it (the sticky status word
@@ -151,8 +160,9 @@ int32_t idlm_isd_paged_attn(const idlm_isd_dims* d, const void* q, const void* k
  *   seed           Philox4x64-10 key word 0; key word 1 is b; counter
  *                  (i,0,0,0) gives u_i (word 0, ratio test) and u'_i (word 1,
  *                  sampling) as (word >> 40) * 2^-24.
- *   T              temperature >= 0; p = softmax(clean/T), q = softmax(mask/T);
- *                  T == 0 is greedy (one-hot argmax, lowest index on ties).
+ *   T              temperature: 0 (greedy: one-hot argmax, lowest index on
+ *                  ties) or 2^-126 <= T < inf; p = softmax(clean/T),
+ *                  q = softmax(mask/T).
  *   out_tokens     [device] int32 [B][N]: kept drafts, then the resampled or
  *                  bonus token, then -1 padding.
  *   out_accept_len [device] int32 [B]: tokens committed, in 1..N.
@@ -160,14 +170,37 @@ int32_t idlm_isd_paged_attn(const idlm_isd_dims* d, const void* q, const void* k
  *                  (p_i(x_i), q_i(x_i), u_i, u'_i) for every draft tested
  *                  (NaN elsewhere); row N holds (sum of sampling weights,
  *                  threshold t, u' used, committed token).
- * Draft i is kept iff p_i(x) >= q_i(x) or u_i*q_i(x) < p_i(x), both in
- * float64.  At the first rejected index j the token is the smallest v whose
- * running sum of w = max(0, p_j - q_j) exceeds t = u'_j * sum(w) (sum(w) == 0
- * falls back to w = p_j); with no rejection w = p_k (bonus row). */
+ * Draft i is kept iff p_i(x) > 0 and (p_i(x) >= q_i(x) or u_i*q_i(x) <
+ * p_i(x)), in float64.  At the first rejected index j the token is the
+ * smallest v whose running sum of w = max(0, p_j - q_j) exceeds
+ * t = u'_j * sum(w) (sum(w) == 0 falls back to w = p_j); with no rejection
+ * w = p_k (bonus row).  The sampling weights, their sums and the row sums
+ * they are normalised by are float64 (exponentials included).
+ * Device-data errors: a draft id outside [-1, V) (that sequence's outputs
+ * are unspecified). */
 int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const void* logits_mask,
                         const int32_t* draft_tokens, uint64_t seed, float T, int32_t* out_tokens,
                         int32_t* out_accept_len, double* out_debug, void* workspace,
                         size_t ws_bytes, void* stream);
+
+/* Debug dump of what the last idlm_isd_accept or idlm_isd_step on
+ * `workspace` computed, with the same sizes, logits and T passed again:
+ *   out_p    [device] double [B][N][V] or NULL: p over the whole vocabulary
+ *            for each clean row, exp((l - M)/T)/S from that call's row
+ *            maximum M and sum S (greedy: one-hot at the argmax), the same
+ *            expression the acceptance evaluates at the drafts.  Rows the
+ *            call did not reduce hold NaN: clean rows past the listed
+ *            drafts, and the bonus row (clean row k) unless it was sampled.
+ *   out_q    [device] double [B][K][V] or NULL: q likewise for MASK rows.
+ *   out_subw [device] double [B][ceil(V/2048)] or NULL: the sampled
+ *            distribution (residual, bonus, or p_j when the residual
+ *            vanished) summed over each 2048-entry sub-chunk and normalised
+ *            to total 1; NaN when greedy.
+ * Reads the workspace only; enqueued on `stream`. */
+int32_t idlm_isd_accept_probs(const idlm_isd_dims* d, const void* logits_clean,
+                              const void* logits_mask, float T, const void* workspace,
+                              size_t ws_bytes, double* out_p, double* out_q, double* out_subw,
+                              void* stream);
 
 /* One ISD step: idlm_isd_paged_attn and idlm_isd_accept, which read
  * different inputs, run side by side: the attention on `stream`, the

@@ -1,4 +1,5 @@
-// isd_accept: the ISD acceptance stage for gfx950.
+// isd_accept: the ISD acceptance stage for gfx950, and the next step's
+// proposals.
 //
 // Clean rows give the anchor distribution p, MASK rows the proposal
 // distribution q; draft x is kept with probability min(1, p(x)/q(x)), which
@@ -7,7 +8,7 @@
 // GeekNews summary, section "Inference & ISD").  The first rejection is
 // resampled from normalize(max(0, p - q)) (the rule under which that
 // guarantee holds) and the committed prefix ends there; with every draft
-// kept, the last clean row supplies a bonus token.
+// kept, clean row k (k = the listed drafts) supplies a bonus token.
 //
 // Three launches; kernel boundaries are the only synchronisation between
 // work-groups (no atomic counters, no fences), and every reduction runs in a
@@ -19,37 +20,42 @@
 //                      any arithmetic and the logits stay packed in registers,
 //                      the slice max is reduced first so each element costs
 //                      one float32 exponential, sums are float64.  The slice
-//                      holding the row's draft also records the draft's
-//                      logit.  The sequence's bonus row (clean row k, k the
-//                      listed drafts) also records each 2048-element
-//                      sub-chunk's sum, relative to the slice max.  Greedy
-//                      (T = 0): (max, lowest argmax).
-//   accept_decide_sum  grid B*S2, S2 sized so the grid fits on the chip at
-//                      once.  In every work-group of a sequence, wave 0 alone
-//                      merges the slices of each row (a lane group per row,
-//                      butterfly reductions), evaluates p_i(x_i) and q_i(x_i)
-//                      in float64 and finds the first rejection with two
-//                      ballots; one barrier hands the plan to the other
+//                      holding the row's draft records the draft's logit.
+//                      Greedy (T = 0): (max, lowest argmax).
+//   accept_decide_sum  grid B*S2.  In every work-group of a sequence, wave 0
+//                      merges the slices of each row, evaluates p_i(x_i) and
+//                      q_i(x_i) in float64 and finds the first rejection with
+//                      two ballots; one barrier hands the plan to the other
 //                      waves.  The first work-group writes the kept prefix,
 //                      the accept length and the plan (the whole answer when
-//                      T = 0).  After a rejection, each work-group sums the
-//                      residual weights max(0, p_j - q_j) of its sub-chunks;
-//                      with every draft kept nothing more is read (the bonus
-//                      row's sub-chunk sums came from accept_stats).
-//   accept_select      grid B, four waves each.  Wave 0 prefixes the
-//                      sub-chunk weights and finds the sub-chunk holding
-//                      t = u' * sum(w); all threads recompute that
-//                      sub-chunk's weights (8 consecutive elements each) and
-//                      a block prefix finds the smallest v whose running sum
-//                      exceeds t.  Where the sub-chunk's own sum and its
-//                      entry in the prefix differ in the last bits, t is
-//                      clamped into the sub-chunk, so the pick is always an
-//                      element with positive weight.
+//                      T = 0).  After a rejection, each work-group sums its
+//                      sub-chunks of the residual pair in float64: all of
+//                      e_p = 2^((l_p - m_p) c) and of e_q (the exact row sums),
+//                      and both over the elements where p > q by the row
+//                      statistics.  With every draft kept it sums the bonus
+//                      row's 2^((l - m) c) per sub-chunk instead.  These
+//                      exponentials are float64 (exp2d).
+//   accept_select      grid B.  The exact ratio S_p/S_q turns the residual
+//                      sums into sub-chunk weights (bonus: the bonus row's
+//                      sub-chunk sums); wave 0 prefixes them and finds the
+//                      sub-chunk holding t = u' * sum(w); all threads rescan
+//                      it in float64 (8 consecutive elements each) and a block
+//                      prefix finds the smallest v whose running sum exceeds
+//                      t.
+//
+// Float64 sampling weights: the token is the smallest v whose running sum of
+// w passes t.  Float32 exponentials move those running sums by ~1e-7 of the
+// total, enough to change the pick in about one draw in a thousand; with
+// float64 exponentials and row sums the pick agrees with an exact evaluation
+// unless t lies within ~1e-14 of a running sum.  The row statistics that
+// decide acceptance stay float32 exponentials summed in float64 (the ratio
+// test needs p(x) and q(x) to ~1e-7, not the running sums of a whole row).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
 #include <algorithm>
 
+#include "isd_exp2d.hpp"
 #include "isd_internal.hpp"
 
 namespace idlm {
@@ -89,13 +95,18 @@ __device__ inline U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uin
 
 __device__ inline double top24(uint64_t w) { return (double)(w >> 40) * 0x1.0p-24; }
 
+struct D4 {
+  double x, y, z, w;
+};
+
 struct AccArgs {
   const void* lc;
   const void* lm;
   const int32_t* drafts;
   uint64_t seed;
-  float c2;      // log2(e) / T  (T > 0)
-  double invT;   // 1 / T        (T > 0)
+  float c2;      // log2(e) / T as float32 (row statistics)
+  double c2d;    // log2(e) / T as float64 (sampling weights)
+  Exp2Coef cf;   // exp2d's coefficients (kept in scalar registers)
   int greedy;    // T == 0
   int32_t* out_tokens;
   int32_t* out_len;
@@ -103,10 +114,11 @@ struct AccArgs {
   int32_t* status;
   double2* stats;   // [B][R][S1]: (m, s) or, greedy, (best value, best index)
   SamplePlan* plan; // [B]
-  double* subsum;   // [B][nsub]
-  float* dlog;      // [B][R]: raw logit of the row's draft (rows that verify or proposed one)
-  double2* bstats;  // [B][nsub]: (max, sum of exp2((l - max) c)) per sub-chunk of the bonus row
+  D4* subsum;       // [B][nsub]: residual pair (S_p, S_q, A, B) or bonus row (E, 0, 0, 0)
+  float* dlog;      // [B][R]: raw logit of the row's draft
   double2* unif;    // [B][16]: (u_i, u'_i) for i = 0..K
+  D4* rowstat;      // [B][R]: (max, sum, kind, scale) for the probability dump
+  double* subw;     // [B][nsub]: normalised sub-chunk sampling weights
   int B, N, K, R, V, S1, nsub, spw, S2, f32;  // spw, S2: chosen at launch
 };
 
@@ -184,13 +196,23 @@ __device__ inline double wave_total(double x) {
   return x;
 }
 
+// 2^((l - m) c) in float64, c = log2(e) / T.
+__device__ inline double wexp(const AccArgs& a, float l, double m) {
+  return exp2d(((double)l - m) * a.c2d, a.cf);
+}
+
+// v[i] for a run-time i in [0, 4), by selects (no indexed register array).
+template <typename T>
+__device__ inline T pick4(const T v[4], int i) {
+  return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 1: row-slice statistics.
 // ---------------------------------------------------------------------------
 template <int U, bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
   __shared__ double sh_s[4];
-  __shared__ double sh_sk[8][4];
   __shared__ float sh_m[4];
   __shared__ int sh_i[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -203,32 +225,19 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
   const int lo = c * kSub * U;
   const int hi = min(a.V, lo + kSub * U);
 
-  // The row's draft (clean row i < K verifies draft i; MASK row i proposed
-  // it; clean row K has none): the thread whose registers hold its logit
-  // records it, so the decision needs no second round of loads.
-  const int di = rho < a.N ? rho : rho - a.N;
-  const int xd = (!a.greedy && di < a.K) ? min(a.drafts[(size_t)b * a.K + di], a.V - 1) : -1;
-  // Clean row kp (kp = the listed drafts, up to the first negative id) is the
-  // row the bonus token comes from when every draft is kept: it also records
-  // each sub-chunk's sum (relative to the slice max), so sampling from it
-  // rescans one sub-chunk instead of re-reading the row.
-  bool bonus = false;
-  if (!a.greedy && rho < a.N) {
-    int kp = a.K;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int id = i < a.K ? a.drafts[(size_t)b * a.K + i] : 0;
-      if (id < 0 && kp == a.K) kp = i;
-    }
-    bonus = rho == kp;
-  }
-
-  // All of this thread's loads first, then the arithmetic.
+  // All of this thread's loads first (they depend on nothing loaded), then
+  // the arithmetic.
   Logits8<VEC, F32> x[U];
 #pragma unroll
   for (int k = 0; k < U; ++k) x[k] = load8<VEC, F32>(row, lo + k * kSub + 8 * tid, hi);
-  // The sequence's uniforms, drawn while the loads are in flight by the
-  // first slice of its first row: thread i <= K draws (u_i, u'_i).
+
+  // The row's draft (clean row i < K verifies draft i; MASK row i proposed
+  // it): the thread whose registers hold its logit records it, so the
+  // decision needs no second round of loads.
+  const int di = rho < a.N ? rho : rho - a.N;
+  const int xd = (!a.greedy && di < a.K) ? min(a.drafts[(size_t)b * a.K + di], a.V - 1) : -1;
+  // The sequence's uniforms, drawn by the first slice of its first row:
+  // thread i <= K draws (u_i, u'_i).
   if (rho == 0 && c == 0 && tid <= a.K) {
     const U64x4 ph = philox4x64_10((uint64_t)tid, 0, 0, 0, a.seed, (uint64_t)b);
     a.unif[(size_t)b * 16 + tid] = make_double2(top24(ph.w[0]), top24(ph.w[1]));
@@ -285,31 +294,19 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
     const float M = fmaxf(fmaxf(sh_m[0], sh_m[1]), fmaxf(sh_m[2], sh_m[3]));
     double s = 0.0;
     if (M != -INFINITY) {
+      // (l - M) is exact (two bf16 values); scaling it by c rounds once.
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) part += __builtin_amdgcn_exp2f((x[k][e] - M) * a.c2);
         s += (double)part;
-        if (bonus) {  // work-group uniform: sub-chunk k's own sum, same exponentials
-          double sk = (double)part;
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) sk += __shfl_xor(sk, off);
-          if (lane == 0) sh_sk[k][wave] = sk;
-        }
       }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
     if (lane == 0) sh_s[wave] = s;
     __syncthreads();
-    if (bonus && tid < U && c * U + tid < a.nsub) {
-      // (slice max, sub-chunk sum relative to it); empty slice: sum 0.
-      const double sk = M == -INFINITY ? 0.0
-                                       : ((sh_sk[tid][0] + sh_sk[tid][1]) + sh_sk[tid][2]) +
-                                             sh_sk[tid][3];
-      a.bstats[(size_t)b * a.nsub + c * U + tid] = make_double2((double)M, sk);
-    }
     if (tid != 0) return;
     res = make_double2((double)M, ((sh_s[0] + sh_s[1]) + sh_s[2]) + sh_s[3]);
   }
@@ -320,12 +317,13 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
 // The sequence's decision, recomputed by every work-group that needs it.
 // Collective: all threads call it; wave 0 does the work.  Leaves the plan in
 // *sh_plan, the draft count in *sh_kp, the per-draft (p, q, u, u') in
-// sh_draft and the raw draft ids in sh_ids.
+// sh_draft, the raw draft ids in sh_ids and each row's (max, sum) in sh_rowM,
+// sh_rowS.
 // ---------------------------------------------------------------------------
 constexpr int kStatCache = 4;  // slice statistics a lane keeps in registers
 
 __device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
-                       double (*sh_draft)[4], int* sh_ids) {
+                       double (*sh_draft)[4], int* sh_ids, double* sh_rowM, double* sh_rowS) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int R = a.R, N = a.N, K = a.K, S1 = a.S1;
@@ -381,20 +379,25 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
         if (row_ok && q + j * L < S1) M = fmax(M, cs[j].x);
       for (int k = q + kStatCache * L; row_ok && k < S1; k += L) M = fmax(M, st[k].x);
       for (int off = 1; off < L; off <<= 1) M = fmax(M, __shfl_xor(M, off));
-      const double c2 = (double)a.c2;
+      const double c2 = (double)a.c2;  // the scale the slice sums were formed with
       S = 0.0;
 #pragma unroll
       for (int j = 0; j < kStatCache; ++j)
         if (row_ok && q + j * L < S1 && cs[j].x != -INFINITY)
-          S += cs[j].y * exp2((cs[j].x - M) * c2);
+          S += cs[j].y * exp2d((cs[j].x - M) * c2, a.cf);
       for (int k = q + kStatCache * L; row_ok && k < S1; k += L) {
         const double2 v = st[k];
-        if (v.x != -INFINITY) S += v.y * exp2((v.x - M) * c2);
+        if (v.x != -INFINITY) S += v.y * exp2d((v.x - M) * c2, a.cf);
       }
       for (int off = 1; off < L; off <<= 1) S += __shfl_xor(S, off);
     }
+    if (q == 0 && row_ok) {
+      sh_rowM[rho] = M;
+      sh_rowS[rho] = S;
+    }
 
-    // Lane i < K: p_i(x_i) from clean row i, q_i(x_i) from MASK row i.
+    // Lane i < K: p_i(x_i) from clean row i, q_i(x_i) from MASK row i, with
+    // the scale of the row sums: 2^((l - M) c) / S.
     const int ia = min(lane, R - 1), ib = min(N + lane, R - 1);
     const double Mp = __shfl(M, ia * L), Sp = __shfl(S, ia * L);
     const double Mq = __shfl(M, ib * L), Sq = __shfl(S, ib * L);
@@ -404,16 +407,18 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
       p = (x == (int)Sp) ? 1.0 : 0.0;
       qq = (x == (int)Sq) ? 1.0 : 0.0;
     } else {
-      p = exp(((double)lpf - Mp) * a.invT) / Sp;
-      qq = exp(((double)lqf - Mq) * a.invT) / Sq;
+      p = exp2d(((double)lpf - Mp) * (double)a.c2, a.cf) / Sp;
+      qq = exp2d(((double)lqf - Mq) * (double)a.c2, a.cf) / Sq;
     }
-    // A negative id ends the list; the first rejection among the listed
-    // drafts ends the kept prefix.
+    // A negative id ends the list.  Draft i is kept iff p > 0 and (p >= q
+    // or u q < p): probability min(1, p/q), and never a token p gives no
+    // mass.  The first rejection among the listed drafts ends the kept
+    // prefix.
     const bool is_draft = lane < K;
     const unsigned long long term = __ballot(is_draft && id < 0);
     const int kp = term ? (int)__builtin_ctzll(term) : K;
-    const bool rej = is_draft && lane < kp && !(p >= qq || u * qq < p);
-    const unsigned long long rm = __ballot(rej);
+    const bool keep = p > 0.0 && (p >= qq || u * qq < p);
+    const unsigned long long rm = __ballot(is_draft && lane < kp && !keep);
     const int j = rm ? (int)__builtin_ctzll(rm) : kp;
 
     const bool resid = j < kp;
@@ -432,12 +437,12 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
       SamplePlan pl;
       pl.mode = a.greedy ? 2 : (resid ? 0 : 1);
       pl.row_p = j;
-      pl.row_q = resid ? j : 0;
       pl.j = j;
+      pl.kp = kp;
       pl.mp = mp;
-      pl.sp = sp_;
       pl.mq = resid ? mq : 0.0;
-      pl.sq = resid ? sq : 1.0;
+      pl.rho = resid ? sp_ / sq : 0.0;
+      pl.sp = sp_;
       pl.u2 = u2j;
       pl.pad = a.greedy ? sp_ : 0.0;  // greedy: the clean argmax of row j
       *sh_plan = pl;
@@ -447,9 +452,11 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
   __syncthreads();
 }
 
-// Writes the kept prefix, accept length, debug rows and (greedy) the token.
+// Writes the kept prefix, accept length, debug rows, row statistics for the
+// probability dump and (greedy) the token.
 __device__ void write_prefix(const AccArgs& a, int b, const SamplePlan& sp, int kp,
-                             double (*sh_draft)[4], const int* sh_ids) {
+                             double (*sh_draft)[4], const int* sh_ids, const double* sh_rowM,
+                             const double* sh_rowS) {
   const int tid = threadIdx.x, N = a.N, j = sp.j;
   if (tid < N) {
     int tok = -1;
@@ -472,117 +479,116 @@ __device__ void write_prefix(const AccArgs& a, int b, const SamplePlan& sp, int 
       const int r = i / 4, k = i % 4;
       double v = NAN;
       if (r < N - 1 && r <= j && r < kp) v = sh_draft[r][k];
-      if (r == N && sp.mode == 2) v = (k == 0) ? 1.0 : (k == 3 ? sp.pad : sp.u2);
+      if (r == N && sp.mode == 2) v = (k == 0) ? 1.0 : (k == 3 ? sp.pad : (k == 2 ? sp.u2 : NAN));
       dbg[i] = v;
     }
   }
+  // Row statistics for the probability dump: the rows of the decision
+  // (clean rows i < k and MASK rows i < k; greedy also clean row k); the
+  // bonus row's statistics come from the sampler.
+  for (int r = tid; r < a.R; r += 256) {
+    const bool used = r < N ? (sp.mode == 2 ? r <= kp : r < kp) : r - N < kp;
+    D4 st;
+    st.x = used ? sh_rowM[r] : NAN;
+    st.y = used ? sh_rowS[r] : NAN;
+    st.z = used ? (sp.mode == 2 ? 2.0 : 1.0) : 0.0;
+    st.w = (double)a.c2;  // the scale of the row sums
+    a.rowstat[(size_t)b * a.R + r] = st;
+  }
+  if (sp.mode == 2)  // greedy: nothing is sampled
+    for (int c = tid; c < a.nsub; c += 256) a.subw[(size_t)b * a.nsub + c] = NAN;
+}
+
+// Block-wide totals of four values per thread, in a fixed order (butterfly
+// in each wave, then the waves in order); valid in every thread after the
+// call.
+__device__ inline void block_total4(double v[4], double (*red)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = wave_total(v[i]);
+  __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][i] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: decision + sub-chunk sums of the sampling weights.
+// Kernel 2: decision + the residual pair's float64 sums per sub-chunk.
 // ---------------------------------------------------------------------------
+#ifndef ACCEPT_SPW
+#define ACCEPT_SPW 4
+#endif
+constexpr int kMaxSpw = ACCEPT_SPW;  // most sub-chunks one summing work-group takes
 
-// Sampling weights of 8 elements, scaled by the p row's sum S_p (sampling is
-// scale-free: t and the running sums scale together).  Mode 1 (p only):
-// w = exp2((l_p - m_p) c).  Mode 0 (residual): w = max(0, e_p - e_q * S_p/S_q)
-// with the ratio applied as a two-float product (hi + lo), so p and q keep
-// the exact relative scale their float64 row sums gave them and the
-// residual carries no systematic float32 scale error; what remains is the
-// per-element rounding of the float32 exponentials.
-template <bool VEC, bool F32>
-__device__ inline void weights8(const AccArgs& a, const SamplePlan& sp, int mode,
-                                const Logits8<VEC, F32>& xp, const Logits8<VEC, F32>& xq,
-                                double w[8]) {
-  const float c2 = a.c2;
-  const float mp = (float)sp.mp;
-  if (mode == 0) {
-    const float mq = (float)sp.mq;
-    const double r = sp.sp / sp.sq;
-    const float r_hi = (float)r;
-    const float r_lo = (float)(r - (double)r_hi);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float ep = __builtin_amdgcn_exp2f((xp[e] - mp) * c2);
-      const float eq = __builtin_amdgcn_exp2f((xq[e] - mq) * c2);
-      w[e] = (double)fmaxf(0.f, ep - fmaf(eq, r_hi, eq * r_lo));
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = (double)__builtin_amdgcn_exp2f((xp[e] - mp) * c2);
-  }
-}
-
-// This thread's sum of its 8 weights, accumulated in a fixed order.
-__device__ inline double thread_sum(const double w[8]) {
-  double ts = 0.0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ts += w[e];
-  return ts;
-}
-
-// Logits v .. v+7 of the p row (and q row, mode 0).
-template <bool VEC, bool F32>
-__device__ inline void load_sub_at(const AccArgs& a, int b, const SamplePlan& sp, int mode, int v,
-                                   Logits8<VEC, F32>& xp, Logits8<VEC, F32>& xq) {
-  xp = load8<VEC, F32>(row_ptr(a, b, sp.row_p), v, a.V);
-  if (mode == 0) {
-    xq = load8<VEC, F32>(row_ptr(a, b, a.N + sp.row_q), v, a.V);
-  } else {
-#pragma unroll
-    for (int e = 0; e < Logits8<VEC, F32>::NW; ++e)
-      xq.w[e] = Logits8<VEC, F32>::kPacked ? 0xFF80FF80u : 0xFF800000u;
-  }
-}
-
-// This thread's 8 logits of sub-chunk sc (thread t: elements 8t .. 8t+7).
-template <bool VEC, bool F32>
-__device__ inline void load_sub(const AccArgs& a, int b, const SamplePlan& sp, int mode, int sc,
-                                Logits8<VEC, F32>& xp, Logits8<VEC, F32>& xq) {
-  load_sub_at<VEC, F32>(a, b, sp, mode, sc * kSub + 8 * (int)threadIdx.x, xp, xq);
-}
-
-constexpr int kMaxSpw = 4;  // most sub-chunks one summing work-group takes
-
-// The decision (recomputed by every work-group of the sequence from the
-// slice statistics and recorded draft logits: one round of loads), then the
-// sub-chunk sums of the sampling weights.  The sequence's first work-group
-// also writes the kept prefix, the accept length and the plan.
 template <bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
   __shared__ double sh_draft[16][4];
   __shared__ int sh_ids[16];
   __shared__ SamplePlan sh_plan;
   __shared__ int sh_kp;
-  __shared__ double sh_wave[kMaxSpw][4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ double sh_rowM[32], sh_rowS[32];
+  __shared__ double sh_red[4][4];
+  const int tid = threadIdx.x;
   const int b = (int)(blockIdx.x / a.S2);
   const int w0 = (int)(blockIdx.x % a.S2);
-  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_ids);
+  decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_ids, sh_rowM, sh_rowS);
   const SamplePlan sp = sh_plan;
   if (w0 == 0) {
-    write_prefix(a, b, sp, sh_kp, sh_draft, sh_ids);
+    write_prefix(a, b, sp, sh_kp, sh_draft, sh_ids, sh_rowM, sh_rowS);
     if (tid == 0) a.plan[b] = sp;
   }
-  // Greedy: the decision already wrote the token.  Bonus row: its sub-chunk
-  // statistics came from the stats pass.
-  if (sp.mode != 0) return;
-
+  // Greedy: the decision already wrote the token.
+  if (sp.mode == 2) return;
+  const bool resid = sp.mode == 0;
   const int sc_lo = w0 * a.spw, n = min(a.nsub - sc_lo, a.spw);
+  const void* rp = row_ptr(a, b, sp.row_p);
+  const void* rq = row_ptr(a, b, a.N + (resid ? sp.row_p : 0));
   Logits8<VEC, F32> xp[kMaxSpw], xq[kMaxSpw];
 #pragma unroll
-  for (int k = 0; k < kMaxSpw; ++k)  // clamped, unconditional: all loads in flight together
-    load_sub<VEC, F32>(a, b, sp, sp.mode, sc_lo + min(k, n - 1), xp[k], xq[k]);
+  for (int k = 0; k < kMaxSpw; ++k) {  // clamped, unconditional: all loads in flight together
+    if (k >= a.spw) break;               // work-group uniform
+    const int v = (sc_lo + min(k, n - 1)) * kSub + 8 * tid;
+    xp[k] = load8<VEC, F32>(rp, v, a.V);
+    if (resid) xq[k] = load8<VEC, F32>(rq, v, a.V);
+  }
 #pragma unroll
   for (int k = 0; k < kMaxSpw; ++k) {
-    double w[8];
-    weights8<VEC, F32>(a, sp, sp.mode, xp[k], xq[k], w);
-    const double tot = wave_total(thread_sum(w));
-    if (lane == 63) sh_wave[k][wave] = tot;
+    if (k >= n) break;  // work-group uniform
+    double v[4] = {0.0, 0.0, 0.0, 0.0};
+    if (resid) {
+      // e_p = 2^((l_p - m_p) c), e_q likewise, relative to the row maxima:
+      // all-element sums (the float64 row sums) and the sums over the
+      // elements where p > q by the row statistics' ratio (A, B; the
+      // sampler forms A - (S_p/S_q) B).
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double ep = wexp(a, xp[k][e], sp.mp);
+        const double eq = wexp(a, xq[k][e], sp.mq);
+        v[0] += ep;
+        v[1] += eq;
+        if (ep > sp.rho * eq) {
+          v[2] += ep;
+          v[3] += eq;
+        }
+      }
+    } else {
+      // Bonus row (clean row k): e = 2^((l - m) c) relative to the row max.
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[0] += wexp(a, xp[k][e], sp.mp);
+    }
+    block_total4(v, sh_red);
+    if (tid == 0) {
+      D4 r;
+      r.x = v[0];
+      r.y = v[1];
+      r.z = v[2];
+      r.w = v[3];
+      a.subsum[(size_t)b * a.nsub + sc_lo + k] = r;
+    }
   }
-  __syncthreads();
-  if (tid < n)
-    a.subsum[(size_t)b * a.nsub + sc_lo + tid] =
-        ((sh_wave[tid][0] + sh_wave[tid][1]) + sh_wave[tid][2]) + sh_wave[tid][3];
 }
 
 // ---------------------------------------------------------------------------
@@ -650,108 +656,95 @@ __device__ void locate(const double* sh_sub, int nsub, double u2, double* sh_W, 
   }
 }
 
-// One work-group (four waves) per sequence.  The sub-chunk weights are staged
-// in LDS and located by wave 0 (locate()); the chosen sub-chunk is then
-// scanned by all 256 threads, thread t owning its elements 8t .. 8t + 7
-// (vocabulary order), under a block prefix of the thread sums.
+// The weight of one rescanned element: residual max(0, e_p - rho e_q),
+// bonus / p-only e_p (relative to the given reference max).
+template <bool VEC, bool F32>
+__device__ inline double elem_w(const AccArgs& a, int mode, const Logits8<VEC, F32>& xp,
+                                const Logits8<VEC, F32>& xq, int e, double mref, double mq,
+                                double rho) {
+  if (mode == 0) return fmax(0.0, wexp(a, xp[e], mref) - rho * wexp(a, xq[e], mq));
+  return wexp(a, xp[e], mref);
+}
+
+// One work-group (four waves) per sequence.  Residual: each thread sums its
+// sub-chunks' (S_p, S_q), the block forms S_p / S_q exactly, and the
+// sub-chunk weights A - (S_p/S_q) B go to LDS; bonus: the bonus row's
+// sub-chunk sums rescaled to its max.  Wave 0 locates t; the chosen
+// sub-chunk is then rescanned in float64 by all 256 threads, thread t owning
+// its elements 8t .. 8t + 7 (vocabulary order), under a block prefix; the
+// thread holding t walks its 8 weights again.
 template <bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
-  __shared__ double sh_sub[kMaxSubChunks];
-  __shared__ float sh_mc[kMaxSubChunks];
+  __shared__ double sh_w[kMaxSubChunks];
+  __shared__ double sh_aux[kMaxSubChunks];
   __shared__ double sh_t, sh_base, sh_W;
   __shared__ int sh_sc, sh_past;
   __shared__ double sh_wsum[4];
   __shared__ int sh_last[4];
   __shared__ int sh_tok;
-  __shared__ float sh_mref;
+  __shared__ double sh_red[4][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   const SamplePlan sp = a.plan[b];
-  // Residual mode samples from the sub-chunk sums of the previous launch,
-  // bonus mode from the bonus row's sub-chunk (max, sum) of the stats pass;
-  // both are loaded with the plan, in one round.
-  const bool from_stats = sp.mode == 1;
-  {
-    const double* subs = a.subsum + (size_t)b * a.nsub;
-    const double2* bs = a.bstats + (size_t)b * a.nsub;
-    for (int i0 = 0; i0 < a.nsub; i0 += 256) {
-      const int i = i0 + tid, ic = min(i, a.nsub - 1);
-      const double sv = subs[ic];
-      const double2 bv = bs[ic];
-      if (i < a.nsub) {
-        sh_sub[i] = from_stats ? bv.y : sv;
-        sh_mc[i] = (float)bv.x;
-      }
-    }
-  }
   if (sp.mode == 2) return;
-  int mode = sp.mode;
+  const int nsub = a.nsub;
+  const bool resid = sp.mode == 0;
+  double rho = 0.0, Sp = 0.0, M = 0.0;
+  if (resid) {
+    // S_p, S_q: float64 sums over every element of the two rows (sub-chunk
+    // order within a thread, then the fixed block order); the sub-chunk
+    // weights A - (S_p/S_q) B.
+    const D4* ss = a.subsum + (size_t)b * nsub;
+    double v[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int c = tid; c < nsub; c += 256) {
+      const D4 r = ss[c];
+      v[0] += r.x;
+      v[1] += r.y;
+      sh_w[c] = r.z;
+      sh_aux[c] = r.w;
+    }
+    block_total4(v, sh_red);
+    Sp = v[0];
+    rho = v[0] / v[1];
+    for (int c = tid; c < nsub; c += 256) sh_w[c] = fmax(0.0, sh_w[c] - rho * sh_aux[c]);
+  } else {
+    // Bonus row: its sub-chunk sums of 2^((l - M) c), M the row max.
+    M = sp.mp;
+    for (int c = tid; c < nsub; c += 256) sh_w[c] = a.subsum[(size_t)b * nsub + c].x;
+  }
   if (tid == 0) sh_tok = -1;
   __syncthreads();
-  if (from_stats) {
-    // Bonus mode: sub-chunk weights s_c * 2^((m_c - M) c), M the row max.
-    if (wave == 0) {
-      float m = -INFINITY;
-      for (int i = lane; i < a.nsub; i += 64) m = fmaxf(m, sh_mc[i]);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      if (lane == 0) sh_mref = m;
-    }
-    __syncthreads();
-    const double mref = sh_mref;
-    for (int i = tid; i < a.nsub; i += 256) {
-      const float m = sh_mc[i];
-      sh_sub[i] = m == -INFINITY ? 0.0 : sh_sub[i] * exp2(((double)m - mref) * (double)a.c2);
-    }
-    __syncthreads();
-  }
-  if (wave == 0) locate(sh_sub, a.nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
+  if (wave == 0) locate(sh_w, nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
   __syncthreads();
-  bool rescale = from_stats;
-  if (!(sh_W > 0.0)) {
-    // The residual vanished to rounding: fall back to p_j over the whole row,
-    // summed per sub-chunk as the summing launch does.
-    mode = 1;
-    rescale = false;
-    for (int sc = 0; sc < a.nsub; ++sc) {
-      Logits8<VEC, F32> xp, xq;
-      load_sub<VEC, F32>(a, b, sp, 1, sc, xp, xq);
-      double w[8];
-      weights8<VEC, F32>(a, sp, 1, xp, xq, w);
-      const double tot = wave_total(thread_sum(w));
-      if (lane == 0) sh_wsum[wave] = tot;
-      __syncthreads();
-      if (tid == 0) sh_sub[sc] = ((sh_wsum[0] + sh_wsum[1]) + sh_wsum[2]) + sh_wsum[3];
-      __syncthreads();
-    }
-    if (wave == 0) locate(sh_sub, a.nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
+  int mode = resid ? 0 : 1;  // 0 residual, 1 bonus, 2 p_j alone (the residual vanished)
+  if (resid && !(sh_W > 0.0)) {
+    // max(0, p_j - q_j) summed to nothing: sample p_j itself, from the
+    // sub-chunk sums of e_p.
+    mode = 2;
+    for (int c = tid; c < nsub; c += 256) sh_w[c] = a.subsum[(size_t)b * nsub + c].x;
+    __syncthreads();
+    if (wave == 0) locate(sh_w, nsub, sp.u2, &sh_W, &sh_t, &sh_base, &sh_sc, &sh_past);
     __syncthreads();
   }
+  const double W = sh_W, tW = sh_t;
   double base = sh_base;
   const int sc = sh_sc, past = sh_past;
   // t sits in [base, base + sum of the sub-chunk) up to rounding at a
   // sub-chunk boundary; clamping it to base keeps it inside.
-  double t = fmax(sh_t, base);
-  SamplePlan ps = sp;
-  if (rescale) {
-    // Scan the bonus sub-chunk with exponentials relative to its own
-    // reference max, as its sum was formed: t moves to that scale, measured
-    // from base.
-    const double f = exp2(((double)sh_mc[sc] - (double)sh_mref) * (double)a.c2);
-    t = (t - base) / f;
-    base = 0.0;
-    ps.mp = sh_mc[sc];
-  }
-  Logits8<VEC, F32> xp, xq;
-  load_sub<VEC, F32>(a, b, ps, mode, sc, xp, xq);
-  double w[8];
-  weights8<VEC, F32>(a, ps, mode, xp, xq, w);
+  double t = fmax(tW, base);
+  const double mref = sp.mp;
   const int v0 = sc * kSub + 8 * tid;
-  const double ls = thread_sum(w);
+  const Logits8<VEC, F32> xp = load8<VEC, F32>(row_ptr(a, b, sp.row_p), v0, a.V);
+  Logits8<VEC, F32> xq;
+  if (mode == 0) xq = load8<VEC, F32>(row_ptr(a, b, a.N + sp.row_p), v0, a.V);
+  double ls = 0.0;
   int lastp = -1;
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (w[e] > 0.0) lastp = v0 + e;
+  for (int e = 0; e < 8; ++e) {
+    const double we = elem_w<VEC, F32>(a, mode, xp, xq, e, mref, sp.mq, rho);
+    ls += we;
+    if (we > 0.0) lastp = v0 + e;
+  }
   // Block prefix: inclusive scan in each wave, then the waves' totals in
   // order.  Thread t owns [base + ex_t, base + inc_t); consecutive threads
   // share their end points exactly (across a wave boundary too: the next
@@ -775,12 +768,13 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   if (lane == 0) ex = woff;
   const double lo = base + ex, hi = base + inc;
   if (!past && lo <= t && t < hi) {
+    // The same weights, in the same order, as the thread sum above.
     double run = lo;
     int tok = lastp;
     bool done = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      run += w[e];
+      run += elem_w<VEC, F32>(a, mode, xp, xq, e, mref, sp.mq, rho);
       if (!done && run > t) {
         tok = v0 + e;
         done = true;
@@ -789,6 +783,8 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
     sh_tok = tok;
   }
   __syncthreads();
+  for (int i = tid; i < nsub; i += 256)  // normalised sub-chunk weights, for the dump
+    a.subw[(size_t)b * nsub + i] = W > 0.0 ? sh_w[i] / W : NAN;
   if (tid == 0) {
     int tok = sh_tok;
     if (tok < 0) {
@@ -798,10 +794,22 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
       if (tok < 0) tok = min(a.V - 1, sc * kSub);
     }
     a.out_tokens[(size_t)b * a.N + sp.j] = tok;
+    // The bonus row's statistics, for the probability dump: (M, W) with W in
+    // units of 2^((l - M) c).
+    if (mode == 1) {
+      D4 st;
+      st.x = M;
+      st.y = W;
+      st.z = 1.0;
+      st.w = a.c2d;
+      a.rowstat[(size_t)b * a.R + sp.kp] = st;
+    }
     if (a.debug) {
+      // (sum of w, t) in probability units, the uniform, the token.
       double* dbg = a.debug + ((size_t)b * (a.N + 1) + a.N) * 4;
-      dbg[0] = sh_W;
-      dbg[1] = sh_t;
+      const double unit = mode == 1 ? W : Sp;
+      dbg[0] = W / unit;
+      dbg[1] = tW / unit;
       dbg[2] = sp.u2;
       dbg[3] = (double)tok;
     }
@@ -815,22 +823,17 @@ int32_t launch_stats(const AccArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
+// Sub-chunks per summing work-group: kMaxSpw (every work-group repeats the
+// decision, and fewer, larger work-groups measured faster at C = 64 while the
+// grid still fits on the chip at once up to about a hundred sequences).
+inline int sums_per_wg(int nsub, bool greedy) { return greedy ? nsub : std::min(kMaxSpw, nsub); }
+
 template <bool VEC, bool F32>
 int32_t launch_all(AccArgs a, hipStream_t s) {
   const int32_t r = launch_stats<kStatsU, VEC, F32>(a, s);
   if (r != IDLM_OK) return r;
-  if (a.greedy) {
-    // One decision work-group per sequence and no sampling.
-    a.spw = a.nsub;
-    a.S2 = 1;
-  } else {
-    // kMaxSpw sub-chunks per work-group: every work-group repeats the
-    // decision, and fewer, larger work-groups measured faster at C = 64
-    // (spw 4: 11.0 us, 3: 12.0 us, 2: 14.4 us) while the grid still fits on
-    // the chip at once up to about a hundred sequences.
-    a.spw = std::min(kMaxSpw, a.nsub);
-    a.S2 = (a.nsub + a.spw - 1) / a.spw;
-  }
+  a.spw = sums_per_wg(a.nsub, a.greedy);
+  a.S2 = (a.nsub + a.spw - 1) / a.spw;
   const int64_t g2 = (int64_t)a.B * a.S2;
   hipLaunchKernelGGL((accept_decide_sum_kernel<VEC, F32>), dim3((unsigned)g2), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
@@ -839,6 +842,127 @@ int32_t launch_all(AccArgs a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Probability dump: p and q over the whole vocabulary from the row
+// statistics the last acceptance left in the workspace, with the expression
+// the decision evaluates at the drafts, 2^((l - M) c) / S.
+// ---------------------------------------------------------------------------
+struct DumpArgs {
+  const void* lc;
+  const void* lm;
+  const D4* rowstat;
+  const double* subw;
+  double* out_p;
+  double* out_q;
+  double* out_subw;
+  Exp2Coef cf;
+  int B, N, K, R, V, nsub, f32, chunks;
+};
+
+__global__ __launch_bounds__(256) void accept_dump_kernel(DumpArgs a) {
+  const int64_t wg = blockIdx.x;
+  const int chunk = (int)(wg % a.chunks);
+  const int64_t br = wg / a.chunks;
+  const int ridx = (int)(br % a.R), b = (int)(br / a.R);
+  double* out = ridx < a.N ? (a.out_p ? a.out_p + ((size_t)b * a.N + ridx) * a.V : nullptr)
+                           : (a.out_q ? a.out_q + ((size_t)b * a.K + (ridx - a.N)) * a.V : nullptr);
+  if (ridx == 0 && chunk == 0 && a.out_subw)
+    for (int i = threadIdx.x; i < a.nsub; i += 256)
+      a.out_subw[(size_t)b * a.nsub + i] = a.subw[(size_t)b * a.nsub + i];
+  if (!out) return;
+  const D4 st = a.rowstat[(size_t)b * a.R + ridx];
+  const size_t es = a.f32 ? 4 : 2;
+  const void* row = ridx < a.N ? (const char*)a.lc + ((size_t)b * a.N + ridx) * a.V * es
+                               : (const char*)a.lm + ((size_t)b * a.K + (ridx - a.N)) * a.V * es;
+  const int kind = (int)st.z;
+  for (int v = chunk * 4096 + threadIdx.x; v < min(a.V, (chunk + 1) * 4096); v += 256) {
+    double pv = NAN;
+    if (kind == 1) pv = exp2d(((double)load1(row, v, a.f32) - st.x) * st.w, a.cf) / st.y;
+    if (kind == 2) pv = v == (int)st.y ? 1.0 : 0.0;
+    out[v] = pv;
+  }
+}
+
+}  // namespace
+
+int64_t accept_max_grid(const idlm_isd_dims& d) {
+  const int R = 2 * d.N - 1;
+  const int64_t S1 = (d.V + (int64_t)kSub * kStatsU - 1) / ((int64_t)kSub * kStatsU);
+  const int nsub = (int)((d.V + kSub - 1) / kSub);
+  const int64_t stats = (int64_t)d.B * R * S1;
+  const int64_t sums = (int64_t)d.B * ((nsub + sums_per_wg(nsub, false) - 1) / sums_per_wg(nsub, false));
+  return std::max(stats, sums);
+}
+
+int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
+                      const int32_t* drafts, uint64_t seed, float T, int32_t* out_tokens,
+                      int32_t* out_len, double* out_debug, char* ws, hipStream_t s) {
+  if (d.B == 0) return IDLM_OK;
+  const AcceptPlan& ap = p.acc;
+  AccArgs a;
+  a.lc = lc;
+  a.lm = lm;
+  a.drafts = drafts;
+  a.seed = seed;
+  a.greedy = (T == 0.0f);
+  a.c2 = a.greedy ? 0.f : (float)(1.4426950408889634 / (double)T);
+  a.c2d = a.greedy ? 0.0 : 1.4426950408889634 / (double)T;
+  a.cf = kExp2Coef;
+  a.out_tokens = out_tokens;
+  a.out_len = out_len;
+  a.debug = out_debug;
+  a.status = (int32_t*)(ws + p.off_status);
+  a.stats = (double2*)(ws + p.off_stats);
+  a.plan = (SamplePlan*)(ws + p.off_splan);
+  a.subsum = (D4*)(ws + p.off_subsum);
+  a.dlog = (float*)(ws + p.off_dlog);
+  a.unif = (double2*)(ws + p.off_unif);
+  a.rowstat = (D4*)(ws + p.off_rowstat);
+  a.subw = (double*)(ws + p.off_subw);
+  a.B = d.B;
+  a.N = d.N;
+  a.K = d.N - 1;
+  a.R = ap.R;
+  a.V = d.V;
+  a.S1 = ap.S1;
+  a.nsub = ap.nsub;
+  a.spw = 1;  // set per launch
+  a.S2 = 1;
+  a.f32 = d.logits_dtype == IDLM_F32;
+  const bool vec = d.V % 8 == 0 && ((uintptr_t)lc % 16) == 0 &&
+                   (lm == nullptr || ((uintptr_t)lm % 16) == 0);
+  if (a.f32) return vec ? launch_all<true, true>(a, s) : launch_all<false, true>(a, s);
+  return vec ? launch_all<true, false>(a, s) : launch_all<false, false>(a, s);
+}
+
+int32_t launch_accept_dump(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
+                           float T, const char* ws, double* out_p, double* out_q,
+                           double* out_subw, hipStream_t s) {
+  (void)T;
+  if (d.B == 0) return IDLM_OK;
+  DumpArgs a;
+  a.lc = lc;
+  a.lm = lm;
+  a.rowstat = (const D4*)(ws + p.off_rowstat);
+  a.subw = (const double*)(ws + p.off_subw);
+  a.out_p = out_p;
+  a.out_q = d.N > 1 ? out_q : nullptr;
+  a.out_subw = out_subw;
+  a.cf = kExp2Coef;
+  a.B = d.B;
+  a.N = d.N;
+  a.K = d.N - 1;
+  a.R = p.acc.R;
+  a.V = d.V;
+  a.nsub = p.acc.nsub;
+  a.f32 = d.logits_dtype == IDLM_F32;
+  a.chunks = (d.V + 4095) / 4096;
+  const int64_t grid = (int64_t)d.B * a.R * a.chunks;
+  hipLaunchKernelGGL(accept_dump_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
+}
+
+namespace {
 // ---------------------------------------------------------------------------
 // Proposals for the next step.
 //
@@ -1119,45 +1243,6 @@ int32_t launch_propose_t(PropArgs a, hipStream_t s) {
 }
 
 }  // namespace
-
-int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
-                      const int32_t* drafts, uint64_t seed, float T, int32_t* out_tokens,
-                      int32_t* out_len, double* out_debug, char* ws, hipStream_t s) {
-  if (d.B == 0) return IDLM_OK;
-  const AcceptPlan& ap = p.acc;
-  AccArgs a;
-  a.lc = lc;
-  a.lm = lm;
-  a.drafts = drafts;
-  a.seed = seed;
-  a.greedy = (T == 0.0f);
-  a.c2 = a.greedy ? 0.f : (float)(1.4426950408889634 / (double)T);
-  a.invT = a.greedy ? 0.0 : 1.0 / (double)T;
-  a.out_tokens = out_tokens;
-  a.out_len = out_len;
-  a.debug = out_debug;
-  a.status = (int32_t*)(ws + p.off_status);
-  a.stats = (double2*)(ws + p.off_stats);
-  a.plan = (SamplePlan*)(ws + p.off_splan);
-  a.subsum = (double*)(ws + p.off_subsum);
-  a.dlog = (float*)(ws + p.off_dlog);
-  a.unif = (double2*)(ws + p.off_unif);
-  a.bstats = (double2*)(ws + p.off_bstats);
-  a.B = d.B;
-  a.N = d.N;
-  a.K = d.N - 1;
-  a.R = ap.R;
-  a.V = d.V;
-  a.S1 = ap.S1;
-  a.nsub = ap.nsub;
-  a.spw = 1;  // set per launch
-  a.S2 = 1;
-  a.f32 = d.logits_dtype == IDLM_F32;
-  const bool vec = d.V % 8 == 0 && ((uintptr_t)lc % 16) == 0 &&
-                   (lm == nullptr || ((uintptr_t)lm % 16) == 0);
-  if (a.f32) return vec ? launch_all<true, true>(a, s) : launch_all<false, true>(a, s);
-  return vec ? launch_all<true, false>(a, s) : launch_all<false, false>(a, s);
-}
 
 }  // namespace idlm
 

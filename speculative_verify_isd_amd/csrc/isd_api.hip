@@ -58,6 +58,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A launch's work-items (work-groups x threads) must fit the 32-bit grid
+// size of a dispatch.
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+bool grid_fits(int64_t groups, int64_t threads) {
+  return groups >= 0 && groups <= kMaxWorkItems / threads;
+}
+
 int32_t check_dims(const idlm_isd_dims* d) {
   if (!d) return IDLM_ERR_NULL;
   if (d->B < 0 || d->B > (1 << 24)) return IDLM_ERR_DIMS;
@@ -73,11 +80,26 @@ int32_t check_dims(const idlm_isd_dims* d) {
   const int64_t R = 2 * (int64_t)d->N - 1;
   if (R * (d->Hq / d->Hkv) > 128) return IDLM_ERR_UNSUPPORTED;
   if ((int64_t)d->B * d->Hkv > (1 << 24)) return IDLM_ERR_DIMS;
+  // Every grid the sizes imply must fit one dispatch: the attention's merge
+  // and float32 kernels (one work-group per (b, KV head)), the acceptance
+  // (greedy and sampled), its probability dump, the proposals and the KV
+  // scatter (one work-item per 8 dims of a row's head).
+  const int64_t B = d->B, K = d->N - 1;
+  const int64_t nsub = ceil_div(d->V, kSub);
+  bool ok = grid_fits(B * d->Hkv, 256);
+  ok = ok && grid_fits(accept_max_grid(*d), 256);
+  ok = ok && grid_fits(B * R * ceil_div(d->V, 4096), 256);
+  ok = ok && grid_fits(B * K * ceil_div(nsub, 8), 256);
+  ok = ok && grid_fits(B * R * d->Hkv * (d->D / 8), 1);
+  if (!ok) return IDLM_ERR_UNSUPPORTED;
   return IDLM_OK;
 }
 
+// T >= 0 and finite; a positive T below the smallest normal float (2^-126)
+// is refused: log2(e)/T, the scale of every exponent, would overflow float32.
 int32_t check_T(float T) {
   if (!(T >= 0.0f) || !isfinite(T)) return IDLM_ERR_TEMPERATURE;
+  if (T > 0.0f && T < 0x1.0p-126f) return IDLM_ERR_TEMPERATURE;
   return IDLM_OK;
 }
 
@@ -104,34 +126,42 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   c.nsub = (int)ceil_div(d.V, kSub);
   c.S1 = (int)ceil_div(d.V, (int64_t)kSub * kStatsU);
   // ---- workspace layout ----
+  // [0, state_end): the sticky status word, the only state kept between
+  // calls (zeroed by workspace_init).  Everything after it is scratch that
+  // every call writes before it reads (launch boundaries order each
+  // hand-over).
   size_t o = 0;
   p->off_status = o;
   o = align256(o + 4);
-  // Streaming attention: two partial-state slots per wave-lane (bf16 path).
+  p->state_end = o;
   // Streaming attention: two partial-state slots per wave-lane (bf16 path).
   const size_t nslots = d.qkv_dtype == IDLM_BF16 ? (size_t)a.max_lanes * 2 : 0;
   p->off_attn_ml = o;
   o = align256(o + nslots * a.RGp * 8);
   p->off_attn_o = o;
   o = align256(o + nslots * a.RGp * d.D * 4);
+  // Acceptance: sampling plans, slice statistics, four sums per sub-chunk
+  // (residual pair, or the bonus row's in .x), draft logits, uniforms; what
+  // the probability dump reads (row statistics, sub-chunk weights).
   p->off_splan = o;
   o = align256(o + (size_t)d.B * sizeof(SamplePlan));
   p->off_stats = o;
   o = align256(o + (size_t)d.B * c.R * c.S1 * 16);
   p->off_subsum = o;
-  o = align256(o + (size_t)d.B * c.nsub * 8);
+  o = align256(o + (size_t)d.B * c.nsub * 32);
   p->off_dlog = o;
   o = align256(o + (size_t)d.B * c.R * 4);
   p->off_unif = o;
   o = align256(o + (size_t)d.B * 16 * 16);
+  p->off_rowstat = o;
+  o = align256(o + (size_t)d.B * c.R * 32);
+  p->off_subw = o;
+  o = align256(o + (size_t)d.B * c.nsub * 8);
   p->off_kv_valid = o;
   o = align256(o + (size_t)d.B);
   // Proposal statistics: (max, sum) per sub-chunk of every next-step MASK row.
   p->off_pstats = o;
   o = align256(o + (size_t)d.B * (d.N - 1) * c.nsub * 16);
-  // Acceptance: (max, sum) per sub-chunk of each sequence's bonus row.
-  p->off_bstats = o;
-  o = align256(o + (size_t)d.B * c.nsub * 16);
   p->total = o;
   return true;
 }
@@ -162,6 +192,12 @@ size_t idlm_isd_workspace_bytes(const idlm_isd_dims* d) {
   Plan p;
   if (!d || !make_plan(*d, &p)) return 0;
   return p.total;
+}
+
+size_t idlm_isd_workspace_state_bytes(const idlm_isd_dims* d) {
+  Plan p;
+  if (!d || !make_plan(*d, &p)) return 0;
+  return p.state_end;
 }
 
 int32_t idlm_isd_validate(const idlm_isd_dims* d, float T) {
@@ -218,6 +254,22 @@ int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const 
                        out_accept_len, out_debug, (char*)workspace, (hipStream_t)stream);
 }
 
+int32_t idlm_isd_accept_probs(const idlm_isd_dims* d, const void* logits_clean,
+                              const void* logits_mask, float T, const void* workspace,
+                              size_t ws_bytes, double* out_p, double* out_q, double* out_subw,
+                              void* stream) {
+  int32_t r = check_dims(d);
+  if (r != IDLM_OK) return r;
+  if ((r = check_T(T)) != IDLM_OK) return r;
+  Plan p;
+  make_plan(*d, &p);
+  if ((r = check_ws(p, (void*)workspace, ws_bytes)) != IDLM_OK) return r;
+  if (d->B == 0) return IDLM_OK;
+  if (!logits_clean || (d->N > 1 && !logits_mask)) return IDLM_ERR_NULL;
+  return launch_accept_dump(*d, p, logits_clean, logits_mask, T, (const char*)workspace, out_p,
+                            out_q, out_subw, (hipStream_t)stream);
+}
+
 int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
                       const int32_t* page_table, const int32_t* ctx_lens,
                       const void* logits_clean, const void* logits_mask,
@@ -241,20 +293,20 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
   ForkSet* f = logits >= kForkMinLogits ? fork_set() : nullptr;
   hipStream_t sa = s;  // the acceptance's stream: the fork, or `stream` itself without one
   if (f) {
-    if (hipEventRecord(f->start, s) != hipSuccess ||
-        hipStreamWaitEvent(f->aux, f->start, 0) != hipSuccess)
-      return IDLM_ERR_HIP;
+    if (hipEventRecord(f->start, s) != hipSuccess) return IDLM_ERR_HIP;
+    if (hipStreamWaitEvent(f->aux, f->start, 0) != hipSuccess) return IDLM_ERR_HIP;
     sa = f->aux;
   }
   r = launch_paged_attn(*d, p, q, kv_pages, page_table, ctx_lens, attn_out, (char*)workspace, s);
-  if (r != IDLM_OK) return r;
-  r = launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
-                    out_accept_len, nullptr, (char*)workspace, sa);
-  if (r != IDLM_OK) return r;
+  if (r == IDLM_OK)
+    r = launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
+                      out_accept_len, nullptr, (char*)workspace, sa);
+  // Join the second stream back whatever happened above, so a failed call
+  // never leaves it forked (a capture in progress stays joined).
   if (f && (hipEventRecord(f->done, f->aux) != hipSuccess ||
-            hipStreamWaitEvent(s, f->done, 0) != hipSuccess))
-    return IDLM_ERR_HIP;
-  return IDLM_OK;
+            hipStreamWaitEvent(s, f->done, 0) != hipSuccess) && r == IDLM_OK)
+    r = IDLM_ERR_HIP;
+  return r;
 }
 
 int32_t idlm_isd_propose(const idlm_isd_dims* d, const void* logits_next,
@@ -280,6 +332,10 @@ static int32_t check_lora(const idlm_isd_lora_dims* L) {
   if ((int64_t)L->B * (2 * L->N - 1) * L->O > (1ll << 31)) return IDLM_ERR_DIMS;
   if (L->H % 32 != 0 || L->H > (1 << 20) || L->rank % 16 != 0 || L->rank > 256)
     return IDLM_ERR_UNSUPPORTED;
+  int64_t items[3];
+  gated_lora_work_items(*L, items);
+  for (int i = 0; i < 3; ++i)
+    if (items[i] > kMaxWorkItems) return IDLM_ERR_UNSUPPORTED;
   return IDLM_OK;
 }
 
@@ -358,7 +414,8 @@ const char* idlm_isd_strerror(int32_t status) {
     case IDLM_ERR_TEMPERATURE: return "temperature must be finite and >= 0";
     case IDLM_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case IDLM_ERR_HIP: return "HIP runtime error";
-    case IDLM_ERR_DEVICE_DATA: return "kernels saw invalid device data (page id, context or draft)";
+    case IDLM_ERR_DEVICE_DATA:
+      return "kernels saw invalid device data (page id, context, draft or free list)";
     default: return "unknown status";
   }
 }

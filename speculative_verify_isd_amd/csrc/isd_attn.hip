@@ -74,6 +74,9 @@ struct AttnArgs {
 
 __device__ inline u16 f32_to_bf16_rne(float f) {
   unsigned u = __float_as_uint(f);
+  // NaN stays NaN (quiet, sign kept); the bias below would carry a NaN
+  // whose payload sits in the low half into infinity or zero.
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u16)(((u >> 16) & 0x8000u) | 0x7FC0u);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (u16)(u >> 16);
 }

@@ -1,0 +1,72 @@
+// exp2d: 2^y in float64 for the acceptance's sampling weights.
+//
+// Written from the mathematics, for host and device alike (the host build is
+// what the CPU tests check against long double):
+//   y = n + f with n = nearest integer to y, |f| <= 1/2 (f exact);
+//   2^f = e^(f ln 2) = sum_k (ln 2)^k f^k / k!, the Taylor series cut after
+//   k = 13: the remainder is below (ln2 / 2)^14 / 14! ~ 4.3e-18 relative;
+//   2^y = 2^f * 2^n by an exponent shift (ldexp).
+// Horner's rule in f with coefficients (ln 2)^k / k! folded at compile time.
+// Accuracy: under one unit in the last place for y in [-1022, 1023]; below
+// that the result goes subnormal and then to 0 (y <= -1075, and -inf); y is
+// clamped into [-1100, 1024] first, so no path branches (a NaN y gives 0).
+//
+// Device code passes the coefficients in as an argument (Exp2Coef, part of
+// the kernel arguments): they then sit in scalar registers and feed the
+// FMAs directly instead of being rebuilt from literals at every use.
+#pragma once
+
+#include <math.h>
+
+#if defined(__HIPCC__)
+#define IDLM_HD __host__ __device__
+#else
+#define IDLM_HD
+#endif
+
+namespace idlm {
+
+namespace exp2d_detail {
+constexpr double kLn2 = 0.693147180559945309417232121458176568;
+constexpr double fact(int k) { return k <= 1 ? 1.0 : k * fact(k - 1); }
+constexpr double ipow(double x, int k) { return k == 0 ? 1.0 : x * ipow(x, k - 1); }
+constexpr double coef(int k) { return ipow(kLn2, k) / fact(k); }
+}  // namespace exp2d_detail
+
+// (ln 2)^k / k!, k = 0..13.
+struct Exp2Coef {
+  double c[14];
+};
+
+constexpr Exp2Coef kExp2Coef = {{1.0, exp2d_detail::coef(1), exp2d_detail::coef(2),
+                                 exp2d_detail::coef(3), exp2d_detail::coef(4),
+                                 exp2d_detail::coef(5), exp2d_detail::coef(6),
+                                 exp2d_detail::coef(7), exp2d_detail::coef(8),
+                                 exp2d_detail::coef(9), exp2d_detail::coef(10),
+                                 exp2d_detail::coef(11), exp2d_detail::coef(12),
+                                 exp2d_detail::coef(13)}};
+
+IDLM_HD inline double exp2d(double y, const Exp2Coef& k) {
+  y = fmin(fmax(y, -1100.0), 1024.0);
+  const double n = rint(y);
+  const double f = y - n;  // exact
+  double p = k.c[13];
+  p = fma(p, f, k.c[12]);
+  p = fma(p, f, k.c[11]);
+  p = fma(p, f, k.c[10]);
+  p = fma(p, f, k.c[9]);
+  p = fma(p, f, k.c[8]);
+  p = fma(p, f, k.c[7]);
+  p = fma(p, f, k.c[6]);
+  p = fma(p, f, k.c[5]);
+  p = fma(p, f, k.c[4]);
+  p = fma(p, f, k.c[3]);
+  p = fma(p, f, k.c[2]);
+  p = fma(p, f, k.c[1]);
+  p = fma(p, f, 1.0);
+  return ldexp(p, (int)n);
+}
+
+IDLM_HD inline double exp2d(double y) { return exp2d(y, kExp2Coef); }
+
+}  // namespace idlm

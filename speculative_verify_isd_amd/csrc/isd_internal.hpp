@@ -43,21 +43,22 @@ struct AttnPlan {
   int max_lanes;  // wave-lanes the partial-state slots are sized for
 };
 
-// How one acceptance launch is cut.
+// How one acceptance call is cut.
 struct AcceptPlan {
   int R;          // rows per sequence: N clean + K mask
   int nsub;       // kSub-element sub-chunks per row
   int S1;         // stats work-groups per row: ceil(V / (kSub * kStatsU))
 };
 
-// Per-sequence hand-over from the ratio test to the sampler.
+// Per-sequence hand-over from the decision to the sampler.
 struct SamplePlan {
-  int32_t mode;    // 0 residual max(0, p_j - q_j), 1 p row only (bonus / fallback), 2 done
-  int32_t row_p;   // clean row holding p
-  int32_t row_q;   // mask row holding q (residual mode)
+  int32_t mode;    // 0 residual max(0, p_j - q_j), 1 bonus row (p only), 2 done (greedy)
+  int32_t row_p;   // clean row holding p (residual: j; bonus: k, the listed drafts)
   int32_t j;       // output index of the sampled token
-  double mp, sp;   // raw-logit max and sum of exp2((l - m) * log2e / T) of row_p
-  double mq, sq;   // same for row_q
+  int32_t kp;      // listed drafts
+  double mp, mq;   // row maxima of clean row j and MASK row j (raw logits)
+  double rho;      // S_p / S_q from the row statistics (splits p > q from p <= q)
+  double sp;       // row sum of clean row j from the row statistics
   double u2;       // sampling uniform
   double pad;
 };
@@ -65,9 +66,11 @@ struct SamplePlan {
 struct Plan {
   AttnPlan attn;
   AcceptPlan acc;
-  size_t off_status, off_attn_ml, off_attn_o;
+  size_t off_status, state_end;  // state kept between calls: [0, state_end)
+  size_t off_attn_ml, off_attn_o;
   size_t off_splan, off_stats, off_subsum, off_dlog, off_unif;
-  size_t off_kv_valid, off_pstats, off_bstats;
+  size_t off_rowstat, off_subw;
+  size_t off_kv_valid, off_pstats;
   size_t total;
 };
 
@@ -81,10 +84,19 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
                       const int32_t* drafts, uint64_t seed, float T, int32_t* out_tokens,
                       int32_t* out_len, double* out_debug, char* ws, hipStream_t s);
 
+// Work-groups of the acceptance's launches (stats, decide + sums, select),
+// the largest of the three.  Host only; shared by validation and launch.
+int64_t accept_max_grid(const idlm_isd_dims& d);
+
+int32_t launch_accept_dump(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
+                           float T, const char* ws, double* out_p, double* out_q,
+                           double* out_subw, hipStream_t s);
+
 int32_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
 
 // Gated LoRA: workspace bytes (split partials and T) and the launcher.
 size_t gated_lora_workspace(const idlm_isd_lora_dims& L);
+void gated_lora_work_items(const idlm_isd_lora_dims& L, int64_t items[3]);
 int32_t launch_gated_lora(const idlm_isd_lora_dims& L, const float* y_base, const void* x,
                           const void* lora_a, const void* lora_b, float scale, void* y_out,
                           char* ws, hipStream_t s);

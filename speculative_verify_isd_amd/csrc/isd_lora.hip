@@ -58,6 +58,9 @@ struct LoraArgs {
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   unsigned u = __float_as_uint(f);
+  // NaN stays NaN (quiet, sign kept); the bias below would carry a NaN
+  // whose payload sits in the low half into infinity or zero.
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
@@ -323,6 +326,20 @@ __global__ __launch_bounds__(256) void lora_up_kernel(LoraArgs a) {
 }
 
 }  // namespace
+
+// Work-items of the three launches for these sizes: down (with the verify
+// rounding groups), partial sum, up.  Host only.
+void gated_lora_work_items(const idlm_isd_lora_dims& L, int64_t items[3]) {
+  const int64_t Mq = (int64_t)L.B * (L.N - 1);
+  const int64_t nrg = (L.rank + 16 * kDownBlocks - 1) / (16 * kDownBlocks);
+  const int64_t rounds = ((int64_t)L.B * L.N * L.O + kRoundPerGroup - 1) / kRoundPerGroup;
+  const int64_t g1 = (Mq + 15) / 16 * nrg * lora_shares(L.H) + rounds;
+  const int64_t gs = (Mq * L.rank / 4 + kSumThreads - 1) / kSumThreads;
+  const int64_t g2 = (Mq + 15) / 16 * ((L.O + 64 * kUpBlocks - 1) / (64 * kUpBlocks));
+  items[0] = g1 * kDownThreads;
+  items[1] = gs * kSumThreads;
+  items[2] = g2 * 256;
+}
 
 size_t gated_lora_workspace(const idlm_isd_lora_dims& L) {
   return (size_t)(lora_shares(L.H) + 1) * L.B * (L.N - 1) * L.rank * sizeof(float);

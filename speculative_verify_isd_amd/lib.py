@@ -34,10 +34,12 @@ STATUS = {
 # Every entry point declared in include/idlm_isd.h.
 ENTRY_POINTS = (
     "idlm_isd_workspace_bytes",
+    "idlm_isd_workspace_state_bytes",
     "idlm_isd_validate",
     "idlm_isd_workspace_init",
     "idlm_isd_paged_attn",
     "idlm_isd_accept",
+    "idlm_isd_accept_probs",
     "idlm_isd_step",
     "idlm_isd_propose",
     "idlm_isd_lora_workspace_bytes",
@@ -92,10 +94,12 @@ def load():
     i32, u64, f32, sz = ctypes.c_int32, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
     sig = {
         "idlm_isd_workspace_bytes": (sz, [D]),
+        "idlm_isd_workspace_state_bytes": (sz, [D]),
         "idlm_isd_validate": (i32, [D, f32]),
         "idlm_isd_workspace_init": (i32, [P, sz, P]),
         "idlm_isd_paged_attn": (i32, [D, P, P, P, P, P, P, sz, P]),
         "idlm_isd_accept": (i32, [D, P, P, P, u64, f32, P, P, P, P, sz, P]),
+        "idlm_isd_accept_probs": (i32, [D, P, P, f32, P, sz, P, P, P, P]),
         "idlm_isd_step": (i32, [D, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, sz, P]),
         "idlm_isd_propose": (i32, [D, P, P, P, u64, f32, P, P, sz, P]),
         "idlm_isd_lora_workspace_bytes": (sz, [ctypes.POINTER(LoraDims)]),
@@ -178,6 +182,7 @@ def _sizes(dims):
         "drafts": B * K,
         "tokens": B * N,
         "debug": B * (N + 1) * 4,
+        "subw": B * ((V + 2047) // 2048),
         "pool": on * dims.num_pages,
         "one": on,
     }
@@ -194,6 +199,10 @@ def _i32():
 
 def idlm_isd_workspace_bytes(dims):
     return int(load().idlm_isd_workspace_bytes(ctypes.byref(dims)))
+
+
+def idlm_isd_workspace_state_bytes(dims):
+    return int(load().idlm_isd_workspace_state_bytes(ctypes.byref(dims)))
 
 
 def idlm_isd_validate(dims, T):
@@ -244,6 +253,22 @@ def idlm_isd_accept(dims, logits_clean, logits_mask, draft_tokens, seed, T, out_
         _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
         _ptr(out_debug, (torch.float64,), "out_debug", allow_none=True, numel=n["debug"]),
         _ptr(ws, (torch.uint8,), "workspace"), ws.numel(), _stream()), "idlm_isd_accept")
+
+
+def idlm_isd_accept_probs(dims, logits_clean, logits_mask, T, ws, out_p=None, out_q=None,
+                          out_subw=None):
+    ft = _fdt(dims.logits_dtype)
+    torch = _torch()
+    n = _sizes(dims)
+    f64 = (torch.float64,)
+    _check(load().idlm_isd_accept_probs(
+        ctypes.byref(dims), _ptr(logits_clean, ft, "logits_clean", numel=n["clean"]),
+        _ptr(logits_mask, ft, "logits_mask", allow_none=True, numel=n["mask"]), float(T),
+        _ptr(ws, (torch.uint8,), "workspace"), ws.numel(),
+        _ptr(out_p, f64, "out_p", allow_none=True, numel=n["clean"]),
+        _ptr(out_q, f64, "out_q", allow_none=True, numel=n["mask"]),
+        _ptr(out_subw, f64, "out_subw", allow_none=True, numel=n["subw"]), _stream()),
+        "idlm_isd_accept_probs")
 
 
 def idlm_isd_step(dims, q, kv_pages, page_table, ctx_lens, logits_clean, logits_mask,
@@ -392,6 +417,19 @@ class DeviceStep:
         idlm_isd_accept(self.dims, self.lc, self.lm, self.drafts,
                         self.w.seed if seed is None else seed, self.w.T if T is None else T,
                         self.tokens, self.lens, self.debug if debug else None, self.ws)
+
+    def probs(self, T=None):
+        """(p [B][N][V], q [B][K][V], sub-chunk weights [B][ceil(V/2048)]) as
+        float64 tensors, dumped from the last accept or step call."""
+        torch = _torch()
+        w = self.w
+        dev = self.lc.device
+        p = torch.empty((w.B, w.N, w.V), dtype=torch.float64, device=dev)
+        q = torch.empty((w.B, max(w.N - 1, 0), w.V), dtype=torch.float64, device=dev)
+        sw = torch.empty((w.B, (w.V + 2047) // 2048), dtype=torch.float64, device=dev)
+        idlm_isd_accept_probs(self.dims, self.lc, self.lm, self.w.T if T is None else T, self.ws,
+                              p, q if w.N > 1 else None, sw)
+        return p, q, sw
 
     def step(self, seed=None, T=None):
         idlm_isd_step(self.dims, self.q, self.kv, self.page_table, self.ctx_lens, self.lc, self.lm,

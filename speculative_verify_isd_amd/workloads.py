@@ -44,10 +44,16 @@ VOCAB = 151936
 
 
 def f32_to_bf16_bits(x):
-    """Round float32 values to bfloat16 (nearest-even) and return the bit patterns."""
+    """Round float32 values to bfloat16 (nearest-even) and return the bit
+    patterns; NaN stays a quiet NaN with its sign (the bias would otherwise
+    carry a NaN whose payload sits in the low half into infinity or zero)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    out = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    if nan.any():
+        out[nan] = ((u[nan] >> np.uint32(16)) & np.uint32(0x8000)).astype(np.uint16) | np.uint16(0x7FC0)
+    return out
 
 
 def _normal_store(rng, shape, scale, dtype, block=1 << 24):

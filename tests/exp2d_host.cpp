@@ -1,0 +1,40 @@
+// Host build of the acceptance's float64 2^y (isd_exp2d.hpp) against long
+// double exp2l: prints the worst relative error over a seeded sweep and the
+// special values, one "name value" pair per line.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "isd_exp2d.hpp"
+
+static uint64_t splitmix(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+int main() {
+  uint64_t s = 12345;
+  double worst = 0.0, worst_y = 0.0;
+  for (int i = 0; i < 2000000; ++i) {
+    const double r = (double)(splitmix(s) >> 11) * 0x1.0p-53;
+    // half the arguments in the sampler's range [-60, 0], half in [-1022, 1023]
+    const double y = (i & 1) ? -60.0 * r : -1022.0 + 2045.0 * r;
+    const long double ref = exp2l((long double)y);
+    const double got = idlm::exp2d(y);
+    const double rel = (double)fabsl(((long double)got - ref) / ref);
+    if (rel > worst) { worst = rel; worst_y = y; }
+  }
+  printf("worst_rel %.6e\nworst_y %.17g\n", worst, worst_y);
+  printf("at_0 %.17g\n", idlm::exp2d(0.0));
+  printf("at_1 %.17g\n", idlm::exp2d(1.0));
+  printf("at_m1 %.17g\n", idlm::exp2d(-1.0));
+  printf("at_half %.17g\n", idlm::exp2d(0.5));
+  printf("at_m1074 %.17g\n", idlm::exp2d(-1074.0));
+  printf("at_m1075 %.17g\n", idlm::exp2d(-1075.5));
+  printf("at_minf %.17g\n", idlm::exp2d(-INFINITY));
+  printf("at_nan %.17g\n", idlm::exp2d(NAN));
+  printf("at_1024 %.17g\n", idlm::exp2d(1024.0));
+  return 0;
+}

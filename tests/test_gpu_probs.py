@@ -1,0 +1,156 @@
+"""GPU parity of whole distributions and of many sampled tokens.
+
+* Every entry of every p and q row the acceptance reduced, dumped through
+  idlm_isd_accept_probs, against the oracle's softmax at 1e-5 absolute, and
+  the sampled distribution (residual, bonus or fallback) summed per
+  2048-entry sub-chunk against the oracle's weight row.  The pages'
+  guarantee that min(1, p/q) acceptance reproduces the autoregressive
+  distribution is a statement about whole rows ("Introspective Diffusion
+  Language Models", section "Inference & ISD").
+* Thousands of residual and bonus draws over 151936-entry rows at
+  sigma = 0.1, where p and q nearly cancel and the residual is the hardest
+  to sample exactly: no committed token may differ from the oracle's unless
+  its threshold lies within the boundary band.
+"""
+
+from concurrent.futures import ThreadPoolExecutor
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle.accept import accept_with_uniforms, num_drafts, softmax_t
+from oracle.dtypes import to_f64
+from oracle.philox import isd_uniforms
+from parity import PROB_TOL, compare_accept, oracle_accept, t32
+from speculative_verify_isd_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SUB = 2048
+SUBW_TOL = 1e-12
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    assert torch.cuda.is_available()
+    return torch
+
+
+def _rows(w, T):
+    """Oracle p rows [B][N][V] and q rows [B][K][V] in float64."""
+    def one(b):
+        P = [softmax_t(to_f64(w.logits_clean[b, i], w.logits_dtype), T) for i in range(w.N)]
+        Q = [softmax_t(to_f64(w.logits_mask[b, i], w.logits_dtype), T) for i in range(w.N - 1)]
+        return P, Q
+    with ThreadPoolExecutor(8) as ex:
+        return list(ex.map(one, range(w.B)))
+
+
+def _sub_sums(x, V):
+    n = (V + SUB - 1) // SUB
+    pad = np.zeros(n * SUB)
+    pad[:V] = x
+    return pad.reshape(n, SUB).sum(axis=1)
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("b16", None), ("c64", None), ("b16", 0.0),
+                                    ("b16", 0.3)])
+def test_full_distributions(torch_cuda, name, T):
+    from speculative_verify_isd_amd.lib import DeviceStep
+
+    w = W.named_workload(name, 1)
+    T = w.T if T is None else T
+    print(f"[case] {w.name} B={w.B} N={w.N} V={w.V} T={T}", flush=True)
+    ds = DeviceStep(w)
+    ds.accept(T=T)
+    p, q, sw = (x.cpu().numpy() for x in ds.probs(T=T))
+    lens = ds.lens.cpu().numpy()
+    _, o_len, infos = oracle_accept(w, T=T)
+    assert np.array_equal(lens, o_len)
+    rows = _rows(w, t32(T))
+    worst, compared = 0.0, 0
+    for b in range(w.B):
+        P, Q = rows[b]
+        info = infos[b]
+        kp = num_drafts(w.draft_tokens[b])
+        bonus = info["mode"].startswith("bonus")
+        for r in range(w.N):
+            used = r < kp or (r == kp and (bonus or T == 0))
+            assert np.isnan(p[b, r]).all() != used, (b, r, used)
+            if used:
+                worst = max(worst, float(np.abs(p[b, r] - P[r]).max()))
+                compared += w.V
+        for r in range(w.N - 1):
+            used = r < kp
+            assert np.isnan(q[b, r]).all() != used, (b, "q", r, used)
+            if used:
+                worst = max(worst, float(np.abs(q[b, r] - Q[r]).max()))
+                compared += w.V
+        if T == 0:
+            assert np.isnan(sw[b]).all()
+            continue
+        ref = _sub_sums(info["w"], w.V)
+        ref = ref / ref.sum()
+        err = float(np.abs(sw[b] - ref).max())
+        assert err < SUBW_TOL, (b, info["mode"], err)
+        assert abs(sw[b].sum() - 1.0) < 1e-12
+    print(f"[probs] {compared} entries, max|dp| {worst:.2e}", flush=True)
+    assert worst < PROB_TOL
+
+
+def _pinned_drafts(w, keep):
+    """Per row the token where p/q is smallest (keep=False: rejected with
+    probability 1 - p/q, about 1/3 at sigma = 0.1) or largest (keep=True:
+    p > q, always kept); p/q is monotone in clean - mask logit."""
+    out = np.empty((w.B, w.N - 1), dtype=np.int32)
+    for b in range(w.B):
+        for i in range(w.N - 1):
+            d = to_f64(w.logits_clean[b, i], w.logits_dtype) - \
+                to_f64(w.logits_mask[b, i], w.logits_dtype)
+            out[b, i] = int(np.argmax(d) if keep else np.argmin(d))
+    return out
+
+
+@pytest.mark.parametrize("mode", ["residual", "bonus"])
+def test_many_draws_sigma_0_1_full_vocabulary(torch_cuda, mode):
+    from speculative_verify_isd_amd.lib import DeviceStep
+
+    B, N, seeds = 64, 8, 64
+    w = W.make_workload(f"draws_{mode}", B=B, N=N, Hq=8, Hkv=8, D=64, V=W.VOCAB,
+                        ctx_lens=[2 * N] * B, T=1.0, seed=91 if mode == "residual" else 92,
+                        sigma=0.1)
+    w = dataclasses.replace(w, draft_tokens=_pinned_drafts(w, keep=(mode == "bonus")))
+    print(f"[case] {w.name} B={B} N={N} V={w.V} sigma=0.1 seeds={seeds}", flush=True)
+    rows = _rows(w, t32(w.T))
+    ds = DeviceStep(w)
+    K = N - 1
+    n_mode, n_boundary = 0, 0
+    for s in range(seeds):
+        seed = 0x5EED0000 + s
+        ds.accept(seed=seed)
+        tokens = ds.tokens.cpu().numpy()
+        lens = ds.lens.cpu().numpy()
+        debug = ds.debug.cpu().numpy()
+
+        def one(b):
+            u, u2 = zip(*(isd_uniforms(seed, b, i) for i in range(N)))
+            n, toks, info = accept_with_uniforms(rows[b][0], rows[b][1],
+                                                 [int(x) for x in w.draft_tokens[b]], u[:K], u2)
+            del info["w"]
+            return n, toks, info
+        with ThreadPoolExecutor(8) as ex:
+            res = list(ex.map(one, range(B)))
+        ref = (np.array([r[1] for r in res], dtype=np.int32),
+               np.array([r[0] for r in res], dtype=np.int32), [r[2] for r in res])
+        n_mode += sum(r[2]["mode"] == mode for r in res)
+        cmp = compare_accept(w, tokens, lens, debug, ref)
+        assert not cmp["bad"], (seed, cmp["bad"])
+        assert cmp["max_prob_err"] < PROB_TOL
+        n_boundary += len(cmp["boundary"])
+    print(f"[draws] {seeds * B} sequences, {n_mode} {mode} draws, boundary {n_boundary}",
+          flush=True)
+    assert n_mode >= (0.8 if mode == "residual" else 1.0) * seeds * B
+    assert n_boundary <= 2
