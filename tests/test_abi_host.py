@@ -261,3 +261,54 @@ def test_binding_checks_every_entry_points_sizes(host_binding):
                               torch.zeros(16 * 64, dtype=bf), torch.zeros(32 * 16 - 1, dtype=bf),
                               0.5, torch.zeros(M * 32, dtype=bf),
                               torch.zeros(64, dtype=torch.uint8))
+
+
+# ---------------------------------------------------------------------------
+# Sizes whose grids would not fit one dispatch, temperatures whose exponent
+# scale would overflow float32, and the workspace's state region.
+# ---------------------------------------------------------------------------
+def test_validate_rejects_grids_beyond_one_dispatch(so):
+    # 2^22 sequences of 7 rows of 8 logits: small in bytes, but the
+    # acceptance's statistics grid would need 7 * 2^22 work-groups of 256.
+    assert L.idlm_isd_validate(L.make_dims(1 << 22, 4, 1, 1, 64, 8, 1, 1), 1.0) == 3
+    assert L.idlm_isd_workspace_bytes(L.make_dims(1 << 22, 4, 1, 1, 64, 8, 1, 1)) == 0
+    assert L.idlm_isd_validate(L.make_dims(1 << 20, 4, 1, 1, 64, 8, 1, 1), 1.0) == 0
+
+
+def test_gated_lora_rejects_grids_beyond_one_dispatch(so):
+    huge = L.LoraDims(1 << 20, 2, 65536, 1, 256)  # down projection: > 2^32 work-items
+    assert L.idlm_isd_lora_workspace_bytes(huge) == 0
+    assert so.idlm_isd_gated_lora(ctypes.byref(huge), None, None, None, None,
+                                  ctypes.c_float(1.0), None, None, 0, None) == 3
+    assert L.idlm_isd_lora_workspace_bytes(L.LoraDims(1 << 20, 2, 4096, 512, 256)) > 0
+
+
+@pytest.mark.parametrize("T,code", [(1e-39, 4), (2.0 ** -127, 4), (2.0 ** -126, 0),
+                                    (3e38, 0), (0.0, 0)])
+def test_temperature_range(so, T, code):
+    # 0 < T < 2^-126 would make log2(e)/T overflow float32; 0 is greedy.
+    assert L.idlm_isd_validate(good(), T) == code
+
+
+def test_workspace_state_bytes(so):
+    d = good()
+    s = so.idlm_isd_workspace_state_bytes(ctypes.byref(d))
+    assert s == 256  # the sticky status word, padded to the workspace alignment
+    assert s < L.idlm_isd_workspace_bytes(d)
+    assert so.idlm_isd_workspace_state_bytes(None) == 0
+    assert so.idlm_isd_workspace_state_bytes(ctypes.byref(good(D=96))) == 0
+
+
+def test_accept_probs_validates_before_launch(so):
+    d = good()
+    n = L.idlm_isd_workspace_bytes(d)
+    fake = ctypes.c_void_p(1 << 20)
+    f = ctypes.c_float
+    assert so.idlm_isd_accept_probs(None, fake, fake, f(1.0), fake, n, fake, fake, fake,
+                                    None) == 1
+    assert so.idlm_isd_accept_probs(ctypes.byref(d), fake, fake, f(-1.0), fake, n, fake, fake,
+                                    fake, None) == 4
+    assert so.idlm_isd_accept_probs(ctypes.byref(d), fake, fake, f(1.0), fake, n - 256, fake,
+                                    fake, fake, None) == 5
+    assert so.idlm_isd_accept_probs(ctypes.byref(d), None, fake, f(1.0), fake, n, fake, fake,
+                                    fake, None) == 1
