@@ -73,14 +73,13 @@ def gather_kv(kv_pages, kv_dtype, page_table_row, ctx, h, D):
     """
     x = chunk_elems(kv_dtype)
     npages = (ctx + PAGE - 1) // PAGE
-    K = np.empty((npages * PAGE, D), dtype=np.float64)
-    V = np.empty((npages * PAGE, D), dtype=np.float64)
-    for p in range(npages):
-        phys = int(page_table_row[p])
-        kblk = to_f64(kv_pages[phys, 0, h], kv_dtype).reshape(D // x, PAGE, x)
-        vblk = to_f64(kv_pages[phys, 1, h], kv_dtype).reshape(D, PAGE)
-        K[p * PAGE:(p + 1) * PAGE] = kblk.transpose(1, 0, 2).reshape(PAGE, D)
-        V[p * PAGE:(p + 1) * PAGE] = vblk.T
+    phys = np.asarray(page_table_row[:npages], dtype=np.int64)  # page p -> physical page
+    # K blocks [page][D/x][16][x] -> [page][slot][D/x][x] = [page*16 + slot][D]
+    kblk = to_f64(kv_pages[phys, 0, h], kv_dtype).reshape(npages, D // x, PAGE, x)
+    K = kblk.transpose(0, 2, 1, 3).reshape(npages * PAGE, D)
+    # V blocks [page][D][16] -> [page][slot][D]
+    vblk = to_f64(kv_pages[phys, 1, h], kv_dtype).reshape(npages, D, PAGE)
+    V = vblk.transpose(0, 2, 1).reshape(npages * PAGE, D)
     return K[:ctx], V[:ctx]
 
 
@@ -100,16 +99,20 @@ def isd_attention(q, kv_pages, page_table, ctx_lens, N, Hkv, kv_dtype):
     for b in range(B):
         ctx = int(ctx_lens[b])
         assert R <= ctx <= PAGE * page_table.shape[1]
+        # Row r sees tokens 0 .. ctx - R + r: the rest of its score row is
+        # masked to -inf (weight exactly 0).  The G query heads of KV head h
+        # (heads h*G .. h*G + G - 1) are evaluated together: score row
+        # r*G + g belongs to row r and query head h*G + g.
+        last = np.repeat(ctx - R + np.arange(R), G)
+        hidden = np.arange(ctx)[None, :] > last[:, None]
         for h in range(Hkv):
             K, V = gather_kv(kv_pages, kv_dtype, page_table[b], ctx, h, D)
-            for g in range(G):
-                hq = h * G + g
-                for r in range(R):
-                    pos = ctx - R + r
-                    scores = K[: pos + 1] @ q[b, r, hq] / math.sqrt(D)
-                    e = np.exp(scores - scores.max())
-                    a = e / e.sum()
-                    out[b, r, hq] = a @ V[: pos + 1]
+            qh = q[b, :, h * G:(h + 1) * G].reshape(R * G, D)
+            scores = qh @ K.T / math.sqrt(D)  # [R*G][ctx]
+            scores[hidden] = -np.inf
+            e = np.exp(scores - scores.max(axis=1, keepdims=True))
+            a = e / e.sum(axis=1, keepdims=True)
+            out[b, :, h * G:(h + 1) * G] = (a @ V).reshape(R, G, D)
     return out
 
 
