@@ -86,3 +86,45 @@ def test_gated_lora_matches_oracle(torch_cuda, B, N, H, O, rank):
         assert exact > 0.98
     else:
         print(f"[lora] N=1: no MASK rows, output is the base rounding", flush=True)
+
+
+def test_gated_lora_nan_and_inf_in_base(torch_cuda):
+    """NaN (quiet, signalling, payload only in the low 16 bits, all ones) and
+    +-Inf in y_base: verify rows round them as the oracle does (NaN keeps
+    its sign as a quiet bf16 NaN, never collapsing to Inf or 0), MASK rows
+    stay NaN / the same infinity after the adapter's finite addition."""
+    torch = torch_cuda
+    from speculative_verify_isd_amd import lib as L
+
+    B, N, H, O, rank = 4, 4, 256, 200, 32
+    M = B * (2 * N - 1)
+    rng = np.random.default_rng(17)
+    x = W.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    a = W.f32_to_bf16_bits((rng.standard_normal((rank, H)) / np.sqrt(H)).astype(np.float32))
+    b = W.f32_to_bf16_bits((0.05 * rng.standard_normal((O, rank))).astype(np.float32))
+    y = rng.standard_normal((M, O)).astype(np.float32)
+    yb = y.view(np.uint32)
+    specials = np.array([0x7FC00000, 0x7F800001, 0xFFFFFFFF, 0x7FFFFFFF, 0xFF800123,
+                         0x7F800000, 0xFF800000], dtype=np.uint32)
+    cells = rng.choice(M * O, size=7 * 12, replace=False)
+    for n, c in enumerate(cells):
+        yb.reshape(-1)[c] = specials[n % len(specials)]
+    ld = L.LoraDims(B, N, H, O, rank)
+    ws = L.alloc_lora_workspace(ld)
+    out = torch.empty((M, O), dtype=torch.bfloat16, device="cuda")
+    L.idlm_isd_gated_lora(ld, torch.from_numpy(y).cuda(), _bf(torch, x), _bf(torch, a),
+                          _bf(torch, b), 2.0, out, ws)
+    torch.cuda.synchronize()
+    got = _bits(out)
+    want = gated_lora(y, x, a, b, 2.0, N)
+    verify = (np.arange(M) % (2 * N - 1)) < N
+    assert np.array_equal(got[verify], want[verify])
+    g = bf16_bits_to_f64(got)
+    w = bf16_bits_to_f64(want)
+    assert np.array_equal(np.isnan(g), np.isnan(w))
+    inf = np.isinf(w)
+    assert inf.sum() > 0 and np.array_equal(g[inf], w[inf])
+    nan_cells = np.isnan(y)
+    assert np.isnan(g[nan_cells]).all()  # every NaN input stays NaN
+    # NaN outputs are the quiet pattern with the input's sign: 0x7FC0 / 0xFFC0
+    assert set(np.unique(got[np.isnan(g)]).tolist()) <= {0x7FC0, 0xFFC0}
