@@ -97,7 +97,8 @@ typedef enum {
   IDLM_ERR_TEMPERATURE = 4, /* T < 0 or not finite */
   IDLM_ERR_WORKSPACE = 5,   /* workspace too small or misaligned */
   IDLM_ERR_HIP = 6,         /* a HIP runtime call failed */
-  IDLM_ERR_DEVICE_DATA = 7  /* kernels saw bad device data (read_status) */
+  IDLM_ERR_DEVICE_DATA = 7, /* kernels saw bad device data (read_status) */
+  IDLM_ERR_SCRATCH = 8      /* sizes exceed idlm_isd_accept_noalloc's scratch */
 } idlm_status;
 
 /* Sizes of one step.  Passed by [host] pointer. */
@@ -201,6 +202,33 @@ int32_t idlm_isd_accept_probs(const idlm_isd_dims* d, const void* logits_clean,
                               const void* logits_mask, float T, const void* workspace,
                               size_t ws_bytes, double* out_p, double* out_q, double* out_subw,
                               void* stream);
+
+/* idlm_isd_accept without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * idlm_isd_accept (bit-identical outputs for the same inputs), except:
+ *   out_status  [device] int32 or NULL: cleared, then set nonzero when the
+ *               kernels see bad device data (a draft id outside [-1, V)).
+ * Scratch: a static device array of IDLM_ISD_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the library's load on that device until the process ends; the
+ * call allocates and frees nothing (no hipMalloc, no allocating library
+ * routine).  The acceptance's buffers take 256 bytes plus seven regions,
+ * each rounded up to a multiple of 256 bytes: B*64, B*R*16*ceil(V/8192),
+ * B*32*ceil(V/2048), B*R*4, B*256, B*R*32 and B*8*ceil(V/2048) (R = 2N-1;
+ * B = 64, N = 4, V = 151936: 0.37 MB; up to B = 1471 at that N and V).
+ * Larger sizes are rejected with IDLM_ERR_SCRATCH before anything is
+ * enqueued.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call clears the one word it needs cleared): calls that
+ * overlap on one GPU (different streams, or host threads without ordering
+ * between them) race and must not be issued.  idlm_isd_accept_probs does
+ * not read this scratch. */
+#define IDLM_ISD_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int32_t idlm_isd_accept_noalloc(const idlm_isd_dims* d, const void* logits_clean,
+                                const void* logits_mask, const int32_t* draft_tokens,
+                                uint64_t seed, float T, int32_t* out_tokens,
+                                int32_t* out_accept_len, double* out_debug, int32_t* out_status,
+                                void* stream);
 
 /* One ISD step: idlm_isd_paged_attn and idlm_isd_accept, which read
  * different inputs, run side by side: the attention on `stream`, the

@@ -896,7 +896,8 @@ int64_t accept_max_grid(const idlm_isd_dims& d) {
 
 int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
                       const int32_t* drafts, uint64_t seed, float T, int32_t* out_tokens,
-                      int32_t* out_len, double* out_debug, char* ws, hipStream_t s) {
+                      int32_t* out_len, double* out_debug, char* ws, hipStream_t s,
+                      int32_t* status) {
   if (d.B == 0) return IDLM_OK;
   const AcceptPlan& ap = p.acc;
   AccArgs a;
@@ -911,7 +912,7 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.out_tokens = out_tokens;
   a.out_len = out_len;
   a.debug = out_debug;
-  a.status = (int32_t*)(ws + p.off_status);
+  a.status = status ? status : (int32_t*)(ws + p.off_status);
   a.stats = (double2*)(ws + p.off_stats);
   a.plan = (SamplePlan*)(ws + p.off_splan);
   a.subsum = (D4*)(ws + p.off_subsum);

@@ -103,6 +103,28 @@ int32_t check_T(float T) {
   return IDLM_OK;
 }
 
+// The acceptance's scratch from offset o on: sampling plans, slice
+// statistics, four sums per sub-chunk (residual pair, or the bonus row's in
+// .x), draft logits, uniforms; what the probability dump reads (row
+// statistics, sub-chunk weights).  Returns the end offset.
+size_t layout_accept(const idlm_isd_dims& d, const AcceptPlan& c, size_t o, Plan* p) {
+  p->off_splan = o;
+  o = align256(o + (size_t)d.B * sizeof(SamplePlan));
+  p->off_stats = o;
+  o = align256(o + (size_t)d.B * c.R * c.S1 * 16);
+  p->off_subsum = o;
+  o = align256(o + (size_t)d.B * c.nsub * 32);
+  p->off_dlog = o;
+  o = align256(o + (size_t)d.B * c.R * 4);
+  p->off_unif = o;
+  o = align256(o + (size_t)d.B * 16 * 16);
+  p->off_rowstat = o;
+  o = align256(o + (size_t)d.B * c.R * 32);
+  p->off_subw = o;
+  o = align256(o + (size_t)d.B * c.nsub * 8);
+  return o;
+}
+
 }  // namespace
 
 bool make_plan(const idlm_isd_dims& d, Plan* p) {
@@ -140,23 +162,7 @@ bool make_plan(const idlm_isd_dims& d, Plan* p) {
   o = align256(o + nslots * a.RGp * 8);
   p->off_attn_o = o;
   o = align256(o + nslots * a.RGp * d.D * 4);
-  // Acceptance: sampling plans, slice statistics, four sums per sub-chunk
-  // (residual pair, or the bonus row's in .x), draft logits, uniforms; what
-  // the probability dump reads (row statistics, sub-chunk weights).
-  p->off_splan = o;
-  o = align256(o + (size_t)d.B * sizeof(SamplePlan));
-  p->off_stats = o;
-  o = align256(o + (size_t)d.B * c.R * c.S1 * 16);
-  p->off_subsum = o;
-  o = align256(o + (size_t)d.B * c.nsub * 32);
-  p->off_dlog = o;
-  o = align256(o + (size_t)d.B * c.R * 4);
-  p->off_unif = o;
-  o = align256(o + (size_t)d.B * 16 * 16);
-  p->off_rowstat = o;
-  o = align256(o + (size_t)d.B * c.R * 32);
-  p->off_subw = o;
-  o = align256(o + (size_t)d.B * c.nsub * 8);
+  o = layout_accept(d, c, o, p);
   p->off_kv_valid = o;
   o = align256(o + (size_t)d.B);
   // Proposal statistics: (max, sum) per sub-chunk of every next-step MASK row.
@@ -171,6 +177,31 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
     p[i] = make_uint4(0, 0, 0, 0);
   if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+// ---- the allocation-free acceptance's scratch ----
+// One static array per GPU: each device that loads the library's code object
+// holds its own copy, at its own address, until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// (with that device current) and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = IDLM_ISD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`.
+int32_t scratch_ptr(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return IDLM_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return IDLM_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return IDLM_OK;
 }
 
 int32_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s) {
@@ -252,6 +283,33 @@ int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const 
   if (d->N > 1 && (!logits_mask || !draft_tokens)) return IDLM_ERR_NULL;
   return launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
                        out_accept_len, out_debug, (char*)workspace, (hipStream_t)stream);
+}
+
+int32_t idlm_isd_accept_noalloc(const idlm_isd_dims* d, const void* logits_clean,
+                                const void* logits_mask, const int32_t* draft_tokens,
+                                uint64_t seed, float T, int32_t* out_tokens,
+                                int32_t* out_accept_len, double* out_debug, int32_t* out_status,
+                                void* stream) {
+  int32_t r = check_dims(d);
+  if (r != IDLM_OK) return r;
+  if ((r = check_T(T)) != IDLM_OK) return r;
+  Plan p;
+  make_plan(*d, &p);
+  // The acceptance's buffers alone, packed after the status word.
+  p.off_status = 0;
+  if (layout_accept(*d, p.acc, 256, &p) > kNoAllocScratchBytes) return IDLM_ERR_SCRATCH;
+  if (d->B == 0) return IDLM_OK;
+  if (!logits_clean || !out_tokens || !out_accept_len) return IDLM_ERR_NULL;
+  if (d->N > 1 && (!logits_mask || !draft_tokens)) return IDLM_ERR_NULL;
+  char* base = nullptr;
+  if ((r = scratch_ptr(&base)) != IDLM_OK) return r;
+  hipStream_t s = (hipStream_t)stream;
+  // The status word is the only scratch read before this call writes it:
+  // cleared by a fill kernel (no memset node under graph capture).
+  int32_t* status = out_status ? out_status : (int32_t*)(base + p.off_status);
+  if ((r = launch_fill_zero(status, sizeof(int32_t), s)) != IDLM_OK) return r;
+  return launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
+                       out_accept_len, out_debug, base, s, status);
 }
 
 int32_t idlm_isd_accept_probs(const idlm_isd_dims* d, const void* logits_clean,
@@ -411,11 +469,13 @@ const char* idlm_isd_strerror(int32_t status) {
     case IDLM_ERR_NULL: return "a required pointer is NULL";
     case IDLM_ERR_DIMS: return "sizes out of range or inconsistent";
     case IDLM_ERR_UNSUPPORTED: return "sizes valid but not supported (D, page size or tile rows)";
-    case IDLM_ERR_TEMPERATURE: return "temperature must be finite and >= 0";
+    case IDLM_ERR_TEMPERATURE: return "temperature must be 0 or finite and >= 2^-126";
     case IDLM_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case IDLM_ERR_HIP: return "HIP runtime error";
     case IDLM_ERR_DEVICE_DATA:
       return "kernels saw invalid device data (page id, context, draft or free list)";
+    case IDLM_ERR_SCRATCH:
+      return "sizes need more than the allocation-free acceptance's static scratch";
     default: return "unknown status";
   }
 }

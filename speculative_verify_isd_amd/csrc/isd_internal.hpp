@@ -80,9 +80,12 @@ int32_t launch_paged_attn(const idlm_isd_dims& d, const Plan& p, const void* q, 
                           const int32_t* page_table, const int32_t* ctx_lens, void* out,
                           char* ws, hipStream_t s);
 
+// The acceptance's buffers are ws + p.off_*; `status` (when not null)
+// replaces the status word at ws + p.off_status.
 int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
                       const int32_t* drafts, uint64_t seed, float T, int32_t* out_tokens,
-                      int32_t* out_len, double* out_debug, char* ws, hipStream_t s);
+                      int32_t* out_len, double* out_debug, char* ws, hipStream_t s,
+                      int32_t* status = nullptr);
 
 // Work-groups of the acceptance's launches (stats, decide + sums, select),
 // the largest of the three.  Host only; shared by validation and launch.

@@ -29,7 +29,11 @@ STATUS = {
     5: "IDLM_ERR_WORKSPACE",
     6: "IDLM_ERR_HIP",
     7: "IDLM_ERR_DEVICE_DATA",
+    8: "IDLM_ERR_SCRATCH",
 }
+
+# idlm_isd_accept_noalloc's static scratch per GPU (IDLM_ISD_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 # Every entry point declared in include/idlm_isd.h.
 ENTRY_POINTS = (
@@ -40,6 +44,7 @@ ENTRY_POINTS = (
     "idlm_isd_paged_attn",
     "idlm_isd_accept",
     "idlm_isd_accept_probs",
+    "idlm_isd_accept_noalloc",
     "idlm_isd_step",
     "idlm_isd_propose",
     "idlm_isd_lora_workspace_bytes",
@@ -100,6 +105,7 @@ def load():
         "idlm_isd_paged_attn": (i32, [D, P, P, P, P, P, P, sz, P]),
         "idlm_isd_accept": (i32, [D, P, P, P, u64, f32, P, P, P, P, sz, P]),
         "idlm_isd_accept_probs": (i32, [D, P, P, f32, P, sz, P, P, P, P]),
+        "idlm_isd_accept_noalloc": (i32, [D, P, P, P, u64, f32, P, P, P, P, P]),
         "idlm_isd_step": (i32, [D, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, sz, P]),
         "idlm_isd_propose": (i32, [D, P, P, P, u64, f32, P, P, sz, P]),
         "idlm_isd_lora_workspace_bytes": (sz, [ctypes.POINTER(LoraDims)]),
@@ -253,6 +259,23 @@ def idlm_isd_accept(dims, logits_clean, logits_mask, draft_tokens, seed, T, out_
         _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
         _ptr(out_debug, (torch.float64,), "out_debug", allow_none=True, numel=n["debug"]),
         _ptr(ws, (torch.uint8,), "workspace"), ws.numel(), _stream()), "idlm_isd_accept")
+
+
+def idlm_isd_accept_noalloc(dims, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
+                            out_accept_len, out_debug=None, out_status=None):
+    ft = _fdt(dims.logits_dtype)
+    torch = _torch()
+    n = _sizes(dims)
+    _check(load().idlm_isd_accept_noalloc(
+        ctypes.byref(dims), _ptr(logits_clean, ft, "logits_clean", numel=n["clean"]),
+        _ptr(logits_mask, ft, "logits_mask", allow_none=True, numel=n["mask"]),
+        _ptr(draft_tokens, _i32(), "draft_tokens", allow_none=True, numel=n["drafts"]),
+        ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), float(T),
+        _ptr(out_tokens, _i32(), "out_tokens", numel=n["tokens"]),
+        _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
+        _ptr(out_debug, (torch.float64,), "out_debug", allow_none=True, numel=n["debug"]),
+        _ptr(out_status, _i32(), "out_status", allow_none=True, numel=1), _stream()),
+        "idlm_isd_accept_noalloc")
 
 
 def idlm_isd_accept_probs(dims, logits_clean, logits_mask, T, ws, out_p=None, out_q=None,

@@ -312,3 +312,34 @@ def test_accept_probs_validates_before_launch(so):
                                     fake, fake, None) == 5
     assert so.idlm_isd_accept_probs(ctypes.byref(d), None, fake, f(1.0), fake, n, fake, fake,
                                     fake, None) == 1
+
+
+def test_accept_noalloc_validates_before_launch(so):
+    fake = ctypes.c_void_p(1 << 20)
+    f = ctypes.c_float
+    d = good()
+    assert so.idlm_isd_accept_noalloc(None, fake, fake, fake, 1, f(1.0), fake, fake, None, None,
+                                      None) == 1
+    assert so.idlm_isd_accept_noalloc(ctypes.byref(d), fake, fake, fake, 1, f(-1.0), fake, fake,
+                                      None, None, None) == 4
+    assert so.idlm_isd_accept_noalloc(ctypes.byref(d), None, fake, fake, 1, f(1.0), fake, fake,
+                                      None, None, None) == 1
+    # The scratch need stated in the header: 256 bytes plus seven regions,
+    # each rounded up to 256 bytes.  Sizes over 8 MiB are refused (8) before
+    # anything is looked up; sizes within it reach the pointer checks (1).
+    def need(B, N=4, V=151936):
+        R, c8, c2 = 2 * N - 1, -(-V // 8192), -(-V // 2048)
+        r = lambda x: -(-x // 256) * 256
+        return 256 + sum(r(x) for x in (B * 64, B * R * 16 * c8, B * 32 * c2, B * R * 4,
+                                         B * 256, B * R * 32, B * 8 * c2))
+    last = max(B for B in range(1, 4096) if need(B) <= L.NOALLOC_SCRATCH_BYTES)
+    assert last == 1471 and need(64) < 400_000
+    for B, code in ((last, 1), (last + 1, 8), (4096, 8)):
+        big = good(B=B)
+        assert L.idlm_isd_validate(big, 1.0) == 0
+        assert so.idlm_isd_accept_noalloc(ctypes.byref(big), None, fake, fake, 1, f(1.0), fake,
+                                          fake, None, None, None) == code
+    assert L.strerror(8) != "unknown status"
+    z = good(B=0)
+    assert so.idlm_isd_accept_noalloc(ctypes.byref(z), None, None, None, 1, f(1.0), None, None,
+                                      None, None, None) == 0
