@@ -196,9 +196,10 @@ __device__ inline double wave_total(double x) {
   return x;
 }
 
-// 2^((l - m) c) in float64, c = log2(e) / T.
-__device__ inline double wexp(const AccArgs& a, float l, double m) {
-  return exp2d(((double)l - m) * a.c2d, a.cf);
+// 2^((l - m) c) in float64, c = log2(e) / T, with exp2t and the
+// work-group's table of 2^(j/64) in LDS.
+__device__ inline double wexp(const AccArgs& a, const double* tab, float l, double m) {
+  return exp2t(((double)l - m) * a.c2d, tab, a.cf);
 }
 
 // v[i] for a run-time i in [0, 4), by selects (no indexed register array).
@@ -531,9 +532,11 @@ __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
   __shared__ int sh_kp;
   __shared__ double sh_rowM[32], sh_rowS[32];
   __shared__ double sh_red[4][4];
+  __shared__ double sh_tab[64];
   const int tid = threadIdx.x;
   const int b = (int)(blockIdx.x / a.S2);
   const int w0 = (int)(blockIdx.x % a.S2);
+  if (tid < 64) sh_tab[tid] = exp2t_entry(tid, a.cf);  // ordered by decide's barrier
   decide(a, b, &sh_plan, &sh_kp, sh_draft, sh_ids, sh_rowM, sh_rowS);
   const SamplePlan sp = sh_plan;
   if (w0 == 0) {
@@ -565,8 +568,8 @@ __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
       // sampler forms A - (S_p/S_q) B).
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const double ep = wexp(a, xp[k][e], sp.mp);
-        const double eq = wexp(a, xq[k][e], sp.mq);
+        const double ep = wexp(a, sh_tab, xp[k][e], sp.mp);
+        const double eq = wexp(a, sh_tab, xq[k][e], sp.mq);
         v[0] += ep;
         v[1] += eq;
         if (ep > sp.rho * eq) {
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
     } else {
       // Bonus row (clean row k): e = 2^((l - m) c) relative to the row max.
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[0] += wexp(a, xp[k][e], sp.mp);
+      for (int e = 0; e < 8; ++e) v[0] += wexp(a, sh_tab, xp[k][e], sp.mp);
     }
     block_total4(v, sh_red);
     if (tid == 0) {
@@ -659,11 +662,11 @@ __device__ void locate(const double* sh_sub, int nsub, double u2, double* sh_W, 
 // The weight of one rescanned element: residual max(0, e_p - rho e_q),
 // bonus / p-only e_p (relative to the given reference max).
 template <bool VEC, bool F32>
-__device__ inline double elem_w(const AccArgs& a, int mode, const Logits8<VEC, F32>& xp,
-                                const Logits8<VEC, F32>& xq, int e, double mref, double mq,
-                                double rho) {
-  if (mode == 0) return fmax(0.0, wexp(a, xp[e], mref) - rho * wexp(a, xq[e], mq));
-  return wexp(a, xp[e], mref);
+__device__ inline double elem_w(const AccArgs& a, const double* tab, int mode,
+                                const Logits8<VEC, F32>& xp, const Logits8<VEC, F32>& xq, int e,
+                                double mref, double mq, double rho) {
+  if (mode == 0) return fmax(0.0, wexp(a, tab, xp[e], mref) - rho * wexp(a, tab, xq[e], mq));
+  return wexp(a, tab, xp[e], mref);
 }
 
 // One work-group (four waves) per sequence.  Residual: each thread sums its
@@ -683,10 +686,12 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   __shared__ int sh_last[4];
   __shared__ int sh_tok;
   __shared__ double sh_red[4][4];
+  __shared__ double sh_tab[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   const SamplePlan sp = a.plan[b];
   if (sp.mode == 2) return;
+  if (tid < 64) sh_tab[tid] = exp2t_entry(tid, a.cf);  // ordered by the barriers below
   const int nsub = a.nsub;
   const bool resid = sp.mode == 0;
   double rho = 0.0, Sp = 0.0, M = 0.0;
@@ -741,7 +746,7 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
   int lastp = -1;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const double we = elem_w<VEC, F32>(a, mode, xp, xq, e, mref, sp.mq, rho);
+    const double we = elem_w<VEC, F32>(a, sh_tab, mode, xp, xq, e, mref, sp.mq, rho);
     ls += we;
     if (we > 0.0) lastp = v0 + e;
   }
@@ -774,7 +779,7 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
     bool done = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      run += elem_w<VEC, F32>(a, mode, xp, xq, e, mref, sp.mq, rho);
+      run += elem_w<VEC, F32>(a, sh_tab, mode, xp, xq, e, mref, sp.mq, rho);
       if (!done && run > t) {
         tok = v0 + e;
         done = true;

@@ -69,4 +69,28 @@ IDLM_HD inline double exp2d(double y, const Exp2Coef& k) {
 
 IDLM_HD inline double exp2d(double y) { return exp2d(y, kExp2Coef); }
 
+// exp2t: the same 2^y from a table, for the sampler's many exponentials:
+//   y = k/64 + r with k the nearest integer to 64 y, |r| <= 1/128 (r exact);
+//   2^y = 2^(k >> 6) * 2^((k & 63)/64) * 2^r, the middle factor from `tab`
+//   (tab[j] = exp2d(j/64), built by exp2t_entry), 2^r by the Taylor series
+//   cut after r^5 (remainder below (ln2/128)^6/6! ~ 3.5e-17 relative).
+// About five fewer arithmetic instructions than exp2d; worst relative error
+// about three units in the last place.  y is clamped into [-1100, 1024]
+// first (a NaN y gives 0).
+IDLM_HD inline double exp2t_entry(int j, const Exp2Coef& k) { return exp2d(j / 64.0, k); }
+
+IDLM_HD inline double exp2t(double y, const double* tab, const Exp2Coef& k) {
+  y = fmin(fmax(y, -1100.0), 1024.0);
+  const double kk = rint(y * 64.0);
+  const double r = fma(kk, -0.015625, y);  // exact
+  const int ki = (int)kk;
+  double p = k.c[5];
+  p = fma(p, r, k.c[4]);
+  p = fma(p, r, k.c[3]);
+  p = fma(p, r, k.c[2]);
+  p = fma(p, r, k.c[1]);
+  p = fma(p, r, 1.0);
+  return ldexp(p * tab[ki & 63], ki >> 6);
+}
+
 }  // namespace idlm

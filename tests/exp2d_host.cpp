@@ -27,6 +27,24 @@ int main() {
     if (rel > worst) { worst = rel; worst_y = y; }
   }
   printf("worst_rel %.6e\nworst_y %.17g\n", worst, worst_y);
+  // exp2t over the same sweep, from its 64-entry table
+  double tab[64];
+  for (int j = 0; j < 64; ++j) tab[j] = idlm::exp2t_entry(j, idlm::kExp2Coef);
+  s = 12345;
+  double worst_t = 0.0;
+  for (int i = 0; i < 2000000; ++i) {
+    const double r = (double)(splitmix(s) >> 11) * 0x1.0p-53;
+    const double y = (i & 1) ? -60.0 * r : -1022.0 + 2045.0 * r;
+    const long double ref = exp2l((long double)y);
+    const double got = idlm::exp2t(y, tab, idlm::kExp2Coef);
+    const double rel = (double)fabsl(((long double)got - ref) / ref);
+    if (rel > worst_t) worst_t = rel;
+  }
+  printf("worst_rel_t %.6e\n", worst_t);
+  printf("t_at_0 %.17g\n", idlm::exp2t(0.0, tab, idlm::kExp2Coef));
+  printf("t_at_m1 %.17g\n", idlm::exp2t(-1.0, tab, idlm::kExp2Coef));
+  printf("t_at_m1075 %.17g\n", idlm::exp2t(-1075.5, tab, idlm::kExp2Coef));
+  printf("t_at_nan %.17g\n", idlm::exp2t(NAN, tab, idlm::kExp2Coef));
   printf("at_0 %.17g\n", idlm::exp2d(0.0));
   printf("at_1 %.17g\n", idlm::exp2d(1.0));
   printf("at_m1 %.17g\n", idlm::exp2d(-1.0));

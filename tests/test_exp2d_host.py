@@ -41,3 +41,10 @@ def test_underflow_and_special_values(results):
     assert results["at_minf"] == 0.0
     assert results["at_nan"] == 0.0               # clamped, never NaN
     assert results["at_1024"] == float("inf")
+
+
+def test_table_variant(results):
+    # exp2t (table of 2^(j/64) and a degree-5 polynomial): a few ulp
+    assert results["worst_rel_t"] < 4.5e-16, results
+    assert results["t_at_0"] == 1.0 and results["t_at_m1"] == 0.5
+    assert results["t_at_m1075"] == 0.0 and results["t_at_nan"] == 0.0
