@@ -241,6 +241,87 @@ def time_propose(ds, w, K):
                         "GB/s": nbytes / (us * 1e-6) / 1e9}}
 
 
+def time_loop(ds, w, K):
+    """The decode loop: each iteration is one step (attention beside the
+    acceptance) whose acceptance takes the MASK-row statistics the previous
+    proposal recorded, then the proposals for the next iteration, which
+    record theirs (two records, alternating).  The workload's MASK rows stand
+    in for every forward's (same shape); each iteration's drafts are the
+    previous proposals, so sequences whose drafts were all kept keep
+    verifying and the others start fresh.  Also the acceptance alone with
+    and without the record on the same drafts (attention call before each,
+    as for the other per-call times)."""
+    import torch
+
+    from speculative_verify_isd_amd import lib as L
+
+    if w.N == 1:
+        return {}
+    K_ = w.N - 1
+    ms = [L.alloc_mask_stats(ds.dims), L.alloc_mask_stats(ds.dims)]
+    d = [torch.full((w.B, K_), -1, dtype=torch.int32, device="cuda"),
+         torch.empty((w.B, K_), dtype=torch.int32, device="cuda")]
+    lens = torch.ones(w.B, dtype=torch.int32, device="cuda")
+    # prime: proposals from a fresh start record the first statistics
+    L.idlm_isd_propose(ds.dims, ds.lm, d[0], lens, 11, w.T, d[1], ds.ws, mask_stats=ms[1])
+    cur = 1
+
+    def iteration(k):
+        nonlocal cur
+        ds.step(seed=100 + k, drafts=d[cur], mask_stats=ms[cur])
+        L.idlm_isd_propose(ds.dims, ds.lm, d[cur], ds.lens, 200 + k, w.T, d[1 - cur], ds.ws,
+                           mask_stats=ms[1 - cur])
+        cur = 1 - cur
+
+    for k in range(5):
+        iteration(k)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(K):
+        iteration(k)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_loop = e0.elapsed_time(e1) / K
+    # committed tokens of K more iterations, counted outside the timed region
+    committed = torch.zeros(1, dtype=torch.int64, device="cuda")
+    for k in range(K):
+        iteration(K + k)
+        committed += ds.lens.sum()
+    torch.cuda.synchronize()
+    assert L.idlm_isd_read_status(ds.ws) == 0
+    tok = float(committed.item())
+
+    # the acceptance alone, with and without the record, on the same drafts
+    times = {}
+    for name, rec in (("with", ms[cur]), ("without", None)):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for k in range(K + 3):
+            ds.attn()
+            e = ev[k - 3] if k >= 3 else None
+            if e:
+                e[0].record()
+            ds.accept(seed=300, debug=False, drafts=d[cur], mask_stats=rec)
+            if e:
+                e[1].record()
+        torch.cuda.synchronize()
+        times[name] = float(np.mean([x[0].elapsed_time(x[1]) for x in ev])) * 1e3
+    assert L.idlm_isd_read_status(ds.ws) == 0
+    lens_np = ds.lens.cpu().numpy()
+    kp = (d[cur].cpu().numpy() >= 0).sum(axis=1)
+    resid = int(((lens_np - 1) < kp).sum())
+    es = 2 if w.logits_dtype == "bf16" else 4
+    nbytes = (w.B * w.N + 2 * resid + (w.B - resid)) * w.V * es + w.B * (w.N + 1) * 4
+    return {"loop": {"ms_per_step": ms_loop, "steps_per_s": 1000.0 / ms_loop,
+                     "committed_tok_per_s": tok / K * 1000.0 / ms_loop,
+                     "mean_accept_len": tok / (K * w.B),
+                     "accept_with_mask_stats_us": times["with"],
+                     "accept_without_mask_stats_us": times["without"],
+                     "accept_with_mask_stats_algorithmic_bytes": nbytes,
+                     "accept_with_mask_stats_GB/s": nbytes / (times["with"] * 1e-6) / 1e9}}
+
+
 def time_lora(ds, w, K, H=4096, O=4096, rank=128):
     """Per-call time of idlm_isd_gated_lora for the workload's rows (B blocks
     of 2N-1) on one projection of a Qwen3-8B-sized layer (H = O = 4096) with a
@@ -462,6 +543,7 @@ def main():
 
     kv = time_kv(ds, w, K)
     kv.update(time_propose(ds, w, K))
+    kv.update(time_loop(ds, w, K))
     kv.update(time_lora(ds, w, K))
 
     lens = ds.lens.cpu().numpy()

@@ -148,6 +148,16 @@ int32_t idlm_isd_paged_attn(const idlm_isd_dims* d, const void* q, const void* k
                             const int32_t* page_table, const int32_t* ctx_lens, void* attn_out,
                             void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of a MASK-row statistics record for these sizes (0 for invalid
+ * sizes).  idlm_isd_propose fills one (its mask_stats argument) with the
+ * statistics of the MASK rows it proposes from and the drafts it makes; the
+ * next step's idlm_isd_accept (or idlm_isd_step) on those drafts takes it
+ * as its mask_stats and then reduces only the N clean rows: in a decode
+ * loop, MASK rows propose with q ("Introspective Diffusion Language
+ * Models", section "Inference & ISD") and that same q tests the drafts one
+ * step later.  Caller-owned device memory, 256-byte aligned.  Host only. */
+size_t idlm_isd_mask_stats_bytes(const idlm_isd_dims* d);
+
 /* Acceptance stage.
  *   logits_clean   [device] [B][N][V] logits_dtype.  Clean row i (i < K)
  *                  gives p_i, which verifies draft i; row K gives the bonus
@@ -171,18 +181,27 @@ int32_t idlm_isd_paged_attn(const idlm_isd_dims* d, const void* q, const void* k
  *                  (p_i(x_i), q_i(x_i), u_i, u'_i) for every draft tested
  *                  (NaN elsewhere); row N holds (sum of sampling weights,
  *                  threshold t, u' used, committed token).
+ *   mask_stats     [device] or NULL: the record idlm_isd_propose wrote when
+ *                  it made draft_tokens from logits_mask at this T.  The MASK
+ *                  rows' maxima and sums and the drafts' logits then come
+ *                  from it, and logits_mask is read only for a rejected
+ *                  draft's residual.  q differs from a reduction of
+ *                  logits_mask by float64 rounding only (the proposals
+ *                  merge their 2048-logit sub-chunks, the acceptance its
+ *                  8192-logit slices).
  * Draft i is kept iff p_i(x) > 0 and (p_i(x) >= q_i(x) or u_i*q_i(x) <
  * p_i(x)), in float64.  At the first rejected index j the token is the
  * smallest v whose running sum of w = max(0, p_j - q_j) exceeds
  * t = u'_j * sum(w) (sum(w) == 0 falls back to w = p_j); with no rejection
  * w = p_k (bonus row).  The sampling weights, their sums and the row sums
  * they are normalised by are float64 (exponentials included).
- * Device-data errors: a draft id outside [-1, V) (that sequence's outputs
- * are unspecified). */
+ * Device-data errors: a draft id outside [-1, V); a mask_stats record made
+ * for other drafts, another T or other sizes (that sequence's outputs are
+ * unspecified). */
 int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const void* logits_mask,
                         const int32_t* draft_tokens, uint64_t seed, float T, int32_t* out_tokens,
-                        int32_t* out_accept_len, double* out_debug, void* workspace,
-                        size_t ws_bytes, void* stream);
+                        int32_t* out_accept_len, double* out_debug, const void* mask_stats,
+                        void* workspace, size_t ws_bytes, void* stream);
 
 /* Debug dump of what the last idlm_isd_accept or idlm_isd_step on
  * `workspace` computed, with the same sizes, logits and T passed again:
@@ -227,8 +246,8 @@ int32_t idlm_isd_accept_probs(const idlm_isd_dims* d, const void* logits_clean,
 int32_t idlm_isd_accept_noalloc(const idlm_isd_dims* d, const void* logits_clean,
                                 const void* logits_mask, const int32_t* draft_tokens,
                                 uint64_t seed, float T, int32_t* out_tokens,
-                                int32_t* out_accept_len, double* out_debug, int32_t* out_status,
-                                void* stream);
+                                int32_t* out_accept_len, double* out_debug,
+                                const void* mask_stats, int32_t* out_status, void* stream);
 
 /* One ISD step: idlm_isd_paged_attn and idlm_isd_accept, which read
  * different inputs, run side by side: the attention on `stream`, the
@@ -240,13 +259,14 @@ int32_t idlm_isd_accept_noalloc(const idlm_isd_dims* d, const void* logits_clean
  * Steps from several host threads on one device share that stream (their
  * enqueues are serialised); while one thread captures a step into a graph,
  * no other thread may run a step on the same device.  N must equal d->N (it
- * is repeated to keep the step's own argument list). */
+ * is repeated to keep the step's own argument list); mask_stats as for
+ * idlm_isd_accept. */
 int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
                       const int32_t* page_table, const int32_t* ctx_lens,
                       const void* logits_clean, const void* logits_mask,
                       const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
                       int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
-                      void* workspace, size_t ws_bytes, void* stream);
+                      const void* mask_stats, void* workspace, size_t ws_bytes, void* stream);
 
 /* Drafts for the next step.  MASK rows propose the next tokens from q
  * ("Introspective Diffusion Language Models", section "Inference & ISD").
@@ -261,11 +281,14 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
  *   draft_tokens [device] int32 [B][K]: this step's list
  *   accept_len   [device] int32 [B]: idlm_isd_accept's output
  *   next_drafts  [device] int32 [B][K], written
+ *   mask_stats   [device] or NULL, written: the MASK rows' statistics and
+ *                the drafts, for the next step's idlm_isd_accept (see
+ *                idlm_isd_mask_stats_bytes)
  * Rows of sequences that start a fresh step are not read. */
 int32_t idlm_isd_propose(const idlm_isd_dims* d, const void* logits_next,
                          const int32_t* draft_tokens, const int32_t* accept_len, uint64_t seed,
-                         float T, int32_t* next_drafts, void* workspace, size_t ws_bytes,
-                         void* stream);
+                         float T, int32_t* next_drafts, void* mask_stats, void* workspace,
+                         size_t ws_bytes, void* stream);
 
 /* Sizes of a gated-LoRA call.  Passed by [host] pointer. */
 typedef struct {

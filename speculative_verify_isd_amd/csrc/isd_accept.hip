@@ -119,6 +119,13 @@ struct AccArgs {
   double2* unif;    // [B][16]: (u_i, u'_i) for i = 0..K
   D4* rowstat;      // [B][R]: (max, sum, kind, scale) for the probability dump
   double* subw;     // [B][nsub]: normalised sub-chunk sampling weights
+  // MASK-row statistics recorded by the proposals that made these drafts
+  // (null: the statistics launch reduces the MASK rows itself).
+  const MaskStatsHeader* mhdr;
+  const double2* mst;     // [B][K]: each MASK row's (max, sum), or greedy (max, argmax)
+  const float* mdlog;     // [B][K]: logit of each proposed draft
+  const int32_t* mtok;    // [B][K]: the proposed drafts
+  int nrows;        // rows the statistics launch reduces per sequence: R, or N with mst
   int B, N, K, R, V, S1, nsub, spw, S2, f32;  // spw, S2: chosen at launch
 };
 
@@ -220,8 +227,8 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(AccArgs a) {
   const int64_t wg = blockIdx.x;
   const int c = (int)(wg % a.S1);
   const int64_t tmp = wg / a.S1;
-  const int rho = (int)(tmp % a.R);
-  const int b = (int)(tmp / a.R);
+  const int rho = (int)(tmp % a.nrows);
+  const int b = (int)(tmp / a.nrows);
   const void* row = row_ptr(a, b, rho);
   const int lo = c * kSub * U;
   const int hi = min(a.V, lo + kSub * U);
@@ -334,20 +341,33 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
     const int L = 64 / rp;
     const int rho = lane / L, q = lane % L;
     const bool row_ok = rho < R;
-    const double2* st = a.stats + ((size_t)b * R + (row_ok ? rho : 0)) * S1;
+    // A row's entries: the statistics launch's slices, or (MASK rows, when
+    // the proposals recorded them) the one (max, sum) the proposals merged.
+    const bool carried = a.mst && row_ok && rho >= N;
+    const double2* st = carried ? a.mst + ((size_t)b * K + (rho - N))
+                                : a.stats + ((size_t)b * R + (row_ok ? rho : 0)) * S1;
+    const int ns = carried ? 1 : S1;
 
     // One round of independent loads: this lane's slice statistics, and for
     // lane i < K draft i and the logits recorded for it.
     double2 cs[kStatCache];
 #pragma unroll
-    for (int j = 0; j < kStatCache; ++j) cs[j] = st[min(q + j * L, S1 - 1)];
+    for (int j = 0; j < kStatCache; ++j) cs[j] = st[min(q + j * L, ns - 1)];
     int id = -1;
     float lpf = 0.f, lqf = 0.f;
     if (K > 0) {
       const int ic = min(lane, K - 1);
       id = a.drafts[(size_t)b * K + ic];
       lpf = a.dlog[(size_t)b * R + ic];
-      lqf = a.dlog[(size_t)b * R + N + ic];
+      lqf = a.mst ? a.mdlog[(size_t)b * K + ic] : a.dlog[(size_t)b * R + N + ic];
+      // The recorded statistics must be the proposals' of these very drafts,
+      // at this temperature and these sizes.
+      if (a.mst && lane < K && id >= 0 &&
+          (a.mtok[(size_t)b * K + ic] != id || a.mhdr->magic != kMaskStatsMagic ||
+           a.mhdr->c2_bits != __float_as_uint(a.c2) || a.mhdr->B != a.B || a.mhdr->K != K ||
+           a.mhdr->V != a.V))
+        __hip_atomic_fetch_or(a.status, kBadMaskStats, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_SYSTEM);
     }
     // Lane i <= K: (u_i, u'_i), drawn by accept_stats.
     const double2 uu = a.unif[(size_t)b * 16 + min(lane, K)];
@@ -361,8 +381,8 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
       int bi = 0x7FFFFFFF;
 #pragma unroll
       for (int j = 0; j < kStatCache; ++j)
-        if (row_ok && q + j * L < S1) better(bv, bi, (float)cs[j].x, (int)cs[j].y);
-      for (int k = q + kStatCache * L; row_ok && k < S1; k += L) {
+        if (row_ok && q + j * L < ns) better(bv, bi, (float)cs[j].x, (int)cs[j].y);
+      for (int k = q + kStatCache * L; row_ok && k < ns; k += L) {
         const double2 v = st[k];
         better(bv, bi, (float)v.x, (int)v.y);
       }
@@ -377,16 +397,16 @@ __device__ void decide(const AccArgs& a, int b, SamplePlan* sh_plan, int* sh_kp,
       M = -INFINITY;
 #pragma unroll
       for (int j = 0; j < kStatCache; ++j)
-        if (row_ok && q + j * L < S1) M = fmax(M, cs[j].x);
-      for (int k = q + kStatCache * L; row_ok && k < S1; k += L) M = fmax(M, st[k].x);
+        if (row_ok && q + j * L < ns) M = fmax(M, cs[j].x);
+      for (int k = q + kStatCache * L; row_ok && k < ns; k += L) M = fmax(M, st[k].x);
       for (int off = 1; off < L; off <<= 1) M = fmax(M, __shfl_xor(M, off));
       const double c2 = (double)a.c2;  // the scale the slice sums were formed with
       S = 0.0;
 #pragma unroll
       for (int j = 0; j < kStatCache; ++j)
-        if (row_ok && q + j * L < S1 && cs[j].x != -INFINITY)
+        if (row_ok && q + j * L < ns && cs[j].x != -INFINITY)
           S += cs[j].y * exp2d((cs[j].x - M) * c2, a.cf);
-      for (int k = q + kStatCache * L; row_ok && k < S1; k += L) {
+      for (int k = q + kStatCache * L; row_ok && k < ns; k += L) {
         const double2 v = st[k];
         if (v.x != -INFINITY) S += v.y * exp2d((v.x - M) * c2, a.cf);
       }
@@ -823,7 +843,7 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AccArgs a) {
 
 template <int U, bool VEC, bool F32>
 int32_t launch_stats(const AccArgs& a, hipStream_t s) {
-  const int64_t g = (int64_t)a.B * a.R * a.S1;
+  const int64_t g = (int64_t)a.B * a.nrows * a.S1;
   hipLaunchKernelGGL((accept_stats_kernel<U, VEC, F32>), dim3((unsigned)g), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
@@ -902,7 +922,7 @@ int64_t accept_max_grid(const idlm_isd_dims& d) {
 int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
                       const int32_t* drafts, uint64_t seed, float T, int32_t* out_tokens,
                       int32_t* out_len, double* out_debug, char* ws, hipStream_t s,
-                      int32_t* status) {
+                      int32_t* status, const void* mstats) {
   if (d.B == 0) return IDLM_OK;
   const AcceptPlan& ap = p.acc;
   AccArgs a;
@@ -925,6 +945,20 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.unif = (double2*)(ws + p.off_unif);
   a.rowstat = (D4*)(ws + p.off_rowstat);
   a.subw = (double*)(ws + p.off_subw);
+  a.mhdr = nullptr;
+  a.mst = nullptr;
+  a.mdlog = nullptr;
+  a.mtok = nullptr;
+  a.nrows = ap.R;
+  if (mstats && d.N > 1) {
+    const MaskStatsLayout ml = mask_stats_layout(d);
+    const char* m = (const char*)mstats;
+    a.mhdr = (const MaskStatsHeader*)m;
+    a.mst = (const double2*)(m + ml.off_st);
+    a.mdlog = (const float*)(m + ml.off_dlog);
+    a.mtok = (const int32_t*)(m + ml.off_tok);
+    a.nrows = d.N;  // the clean rows only
+  }
   a.B = d.B;
   a.N = d.N;
   a.K = d.N - 1;
@@ -995,10 +1029,35 @@ struct PropArgs {
   const int32_t* accept_len;
   int32_t* next;            // [B][K]
   double2* st;              // [B][K][nsub]
+  MaskStatsHeader* mhdr;    // with the next three: the MASK-row statistics record, or null
+  double2* mrow;            // [B][K]: each row's (max, sum) or greedy (max, argmax)
+  float* mdlog;             // [B][K]
+  int32_t* mtok;            // [B][K]
   uint64_t seed;
   float c2;                 // log2(e) / T
   int greedy, B, K, V, nsub, f32;
 };
+
+// Thread 0 of each (b, i) work-group: the draft, and in the MASK-row
+// statistics record its logit and the record's header.
+__device__ inline void put_draft(const PropArgs& a, int b, int i, int tok) {
+  a.next[(size_t)b * a.K + i] = tok;
+  if (!a.mtok) return;
+  a.mtok[(size_t)b * a.K + i] = tok;
+  const size_t es = a.f32 ? 4 : 2;
+  const void* row = (const char*)a.ln + ((size_t)b * a.K + i) * a.V * es;
+  a.mdlog[(size_t)b * a.K + i] = tok >= 0 ? load1(row, tok, a.f32) : 0.f;
+  if (b == 0 && i == 0) {
+    MaskStatsHeader h;
+    h.magic = kMaskStatsMagic;
+    h.c2_bits = __float_as_uint(a.c2);
+    h.B = a.B;
+    h.K = a.K;
+    h.V = a.V;
+    h.nsub = a.nsub;
+    *a.mhdr = h;
+  }
+}
 
 constexpr int kPropSubPerWave = 2;
 
@@ -1093,9 +1152,8 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
   __shared__ int sh_last[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x / a.K, i = blockIdx.x % a.K;
-  int32_t* dst = a.next + (size_t)b * a.K + i;
   if (!continues(a, b)) {
-    if (tid == 0) *dst = -1;
+    if (tid == 0) put_draft(a, b, i, -1);
     return;
   }
   const double2* st = a.st + ((size_t)b * a.K + i) * a.nsub;
@@ -1112,7 +1170,10 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
       const int io = __shfl_xor(bi, off);
       better(bv, bi, vo, io);
     }
-    if (lane == 0) *dst = bi == 0x7FFFFFFF ? 0 : bi;
+    if (lane == 0) {
+      put_draft(a, b, i, bi == 0x7FFFFFFF ? 0 : bi);
+      if (a.mrow) a.mrow[(size_t)b * a.K + i] = make_double2((double)bv, (double)bi);
+    }
     return;
   }
   if (wave == 0) {
@@ -1175,6 +1236,7 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
       sh_past = past;
       sh_mc = (float)st[sc].x;
       sh_tok = -1;
+      if (a.mrow) a.mrow[(size_t)b * a.K + i] = make_double2(M, W);  // the row's (max, sum)
     }
   }
   __syncthreads();
@@ -1232,7 +1294,7 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
   if (tid == 0) {
     int tok = sh_tok;
     for (int q = 3; q >= 0 && tok < 0; --q) tok = sh_last[q];
-    *dst = tok < 0 ? min(a.V - 1, sc * kSub) : tok;
+    put_draft(a, b, i, tok < 0 ? min(a.V - 1, sc * kSub) : tok);
   }
 }
 
@@ -1256,7 +1318,7 @@ namespace idlm {
 
 int32_t launch_propose(const idlm_isd_dims& d, const Plan& p, const void* logits_next,
                        const int32_t* drafts, const int32_t* accept_len, uint64_t seed, float T,
-                       int32_t* next_drafts, char* ws, hipStream_t s) {
+                       int32_t* next_drafts, char* ws, hipStream_t s, void* mstats) {
   if (d.B == 0 || d.N == 1) return IDLM_OK;
   PropArgs a = {};
   a.ln = logits_next;
@@ -1264,6 +1326,14 @@ int32_t launch_propose(const idlm_isd_dims& d, const Plan& p, const void* logits
   a.accept_len = accept_len;
   a.next = next_drafts;
   a.st = (double2*)(ws + p.off_pstats);
+  if (mstats) {
+    const MaskStatsLayout ml = mask_stats_layout(d);
+    char* m = (char*)mstats;
+    a.mhdr = (MaskStatsHeader*)m;
+    a.mrow = (double2*)(m + ml.off_st);
+    a.mdlog = (float*)(m + ml.off_dlog);
+    a.mtok = (int32_t*)(m + ml.off_tok);
+  }
   a.seed = seed;
   a.greedy = (T == 0.0f);
   a.c2 = a.greedy ? 0.f : (float)(1.4426950408889634 / (double)T);

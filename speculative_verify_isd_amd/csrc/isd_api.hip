@@ -127,6 +127,16 @@ size_t layout_accept(const idlm_isd_dims& d, const AcceptPlan& c, size_t o, Plan
 
 }  // namespace
 
+MaskStatsLayout mask_stats_layout(const idlm_isd_dims& d) {
+  MaskStatsLayout m;
+  const size_t BK = (size_t)d.B * (d.N - 1);
+  m.off_st = 256;
+  m.off_dlog = align256(m.off_st + BK * 16);
+  m.off_tok = align256(m.off_dlog + BK * 4);
+  m.total = align256(m.off_tok + BK * 4);
+  return m;
+}
+
 bool make_plan(const idlm_isd_dims& d, Plan* p) {
   if (check_dims(&d) != IDLM_OK) return false;
   memset(p, 0, sizeof(*p));
@@ -231,6 +241,11 @@ size_t idlm_isd_workspace_state_bytes(const idlm_isd_dims* d) {
   return p.state_end;
 }
 
+size_t idlm_isd_mask_stats_bytes(const idlm_isd_dims* d) {
+  if (!d || check_dims(d) != IDLM_OK) return 0;
+  return mask_stats_layout(*d).total;
+}
+
 int32_t idlm_isd_validate(const idlm_isd_dims* d, float T) {
   const int32_t r = check_dims(d);
   if (r != IDLM_OK) return r;
@@ -270,26 +285,28 @@ int32_t idlm_isd_paged_attn(const idlm_isd_dims* d, const void* q, const void* k
 
 int32_t idlm_isd_accept(const idlm_isd_dims* d, const void* logits_clean, const void* logits_mask,
                         const int32_t* draft_tokens, uint64_t seed, float T, int32_t* out_tokens,
-                        int32_t* out_accept_len, double* out_debug, void* workspace,
-                        size_t ws_bytes, void* stream) {
+                        int32_t* out_accept_len, double* out_debug, const void* mask_stats,
+                        void* workspace, size_t ws_bytes, void* stream) {
   int32_t r = check_dims(d);
   if (r != IDLM_OK) return r;
   if ((r = check_T(T)) != IDLM_OK) return r;
   Plan p;
   make_plan(*d, &p);
   if ((r = check_ws(p, workspace, ws_bytes)) != IDLM_OK) return r;
+  if (((uintptr_t)mask_stats & 255) != 0) return IDLM_ERR_WORKSPACE;
   if (d->B == 0) return IDLM_OK;
   if (!logits_clean || !out_tokens || !out_accept_len) return IDLM_ERR_NULL;
   if (d->N > 1 && (!logits_mask || !draft_tokens)) return IDLM_ERR_NULL;
   return launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
-                       out_accept_len, out_debug, (char*)workspace, (hipStream_t)stream);
+                       out_accept_len, out_debug, (char*)workspace, (hipStream_t)stream,
+                       nullptr, mask_stats);
 }
 
 int32_t idlm_isd_accept_noalloc(const idlm_isd_dims* d, const void* logits_clean,
                                 const void* logits_mask, const int32_t* draft_tokens,
                                 uint64_t seed, float T, int32_t* out_tokens,
-                                int32_t* out_accept_len, double* out_debug, int32_t* out_status,
-                                void* stream) {
+                                int32_t* out_accept_len, double* out_debug,
+                                const void* mask_stats, int32_t* out_status, void* stream) {
   int32_t r = check_dims(d);
   if (r != IDLM_OK) return r;
   if ((r = check_T(T)) != IDLM_OK) return r;
@@ -298,6 +315,7 @@ int32_t idlm_isd_accept_noalloc(const idlm_isd_dims* d, const void* logits_clean
   // The acceptance's buffers alone, packed after the status word.
   p.off_status = 0;
   if (layout_accept(*d, p.acc, 256, &p) > kNoAllocScratchBytes) return IDLM_ERR_SCRATCH;
+  if (((uintptr_t)mask_stats & 255) != 0) return IDLM_ERR_WORKSPACE;
   if (d->B == 0) return IDLM_OK;
   if (!logits_clean || !out_tokens || !out_accept_len) return IDLM_ERR_NULL;
   if (d->N > 1 && (!logits_mask || !draft_tokens)) return IDLM_ERR_NULL;
@@ -309,7 +327,7 @@ int32_t idlm_isd_accept_noalloc(const idlm_isd_dims* d, const void* logits_clean
   int32_t* status = out_status ? out_status : (int32_t*)(base + p.off_status);
   if ((r = launch_fill_zero(status, sizeof(int32_t), s)) != IDLM_OK) return r;
   return launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
-                       out_accept_len, out_debug, base, s, status);
+                       out_accept_len, out_debug, base, s, status, mask_stats);
 }
 
 int32_t idlm_isd_accept_probs(const idlm_isd_dims* d, const void* logits_clean,
@@ -333,7 +351,7 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
                       const void* logits_clean, const void* logits_mask,
                       const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
                       int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
-                      void* workspace, size_t ws_bytes, void* stream) {
+                      const void* mask_stats, void* workspace, size_t ws_bytes, void* stream) {
   int32_t r = check_dims(d);
   if (r != IDLM_OK) return r;
   if (N != d->N) return IDLM_ERR_DIMS;
@@ -341,6 +359,7 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
   Plan p;
   make_plan(*d, &p);
   if ((r = check_ws(p, workspace, ws_bytes)) != IDLM_OK) return r;
+  if (((uintptr_t)mask_stats & 255) != 0) return IDLM_ERR_WORKSPACE;
   if (d->B == 0) return IDLM_OK;
   if (!q || !kv_pages || !page_table || !ctx_lens || !attn_out) return IDLM_ERR_NULL;
   if (!logits_clean || !out_tokens || !out_accept_len) return IDLM_ERR_NULL;
@@ -358,7 +377,7 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
   r = launch_paged_attn(*d, p, q, kv_pages, page_table, ctx_lens, attn_out, (char*)workspace, s);
   if (r == IDLM_OK)
     r = launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
-                      out_accept_len, nullptr, (char*)workspace, sa);
+                      out_accept_len, nullptr, (char*)workspace, sa, nullptr, mask_stats);
   // Join the second stream back whatever happened above, so a failed call
   // never leaves it forked (a capture in progress stays joined).
   if (f && (hipEventRecord(f->done, f->aux) != hipSuccess ||
@@ -369,18 +388,19 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
 
 int32_t idlm_isd_propose(const idlm_isd_dims* d, const void* logits_next,
                          const int32_t* draft_tokens, const int32_t* accept_len, uint64_t seed,
-                         float T, int32_t* next_drafts, void* workspace, size_t ws_bytes,
-                         void* stream) {
+                         float T, int32_t* next_drafts, void* mask_stats, void* workspace,
+                         size_t ws_bytes, void* stream) {
   int32_t r = check_dims(d);
   if (r != IDLM_OK) return r;
   if ((r = check_T(T)) != IDLM_OK) return r;
   Plan p;
   make_plan(*d, &p);
   if ((r = check_ws(p, workspace, ws_bytes)) != IDLM_OK) return r;
+  if (((uintptr_t)mask_stats & 255) != 0) return IDLM_ERR_WORKSPACE;
   if (d->B == 0 || d->N == 1) return IDLM_OK;
   if (!logits_next || !draft_tokens || !accept_len || !next_drafts) return IDLM_ERR_NULL;
   return launch_propose(*d, p, logits_next, draft_tokens, accept_len, seed, T, next_drafts,
-                        (char*)workspace, (hipStream_t)stream);
+                        (char*)workspace, (hipStream_t)stream, mask_stats);
 }
 
 static int32_t check_lora(const idlm_isd_lora_dims* L) {

@@ -31,7 +31,30 @@ constexpr int kMinRunPages = MIN_RUN_PAGES_DEFAULT;  // shortest run of pages gi
 constexpr int kRingPages = RING_PAGES_DEFAULT;  // page buffers per attention wave (D = 128)
 
 // Sticky device status bits (workspace word 0).
-enum : int32_t { kBadPage = 1, kBadCtx = 2, kBadDraft = 4, kFreeList = 8, kBadLen = 16 };
+enum : int32_t {
+  kBadPage = 1,
+  kBadCtx = 2,
+  kBadDraft = 4,
+  kFreeList = 8,
+  kBadLen = 16,
+  kBadMaskStats = 32
+};
+
+// MASK-row statistics that idlm_isd_propose records for the acceptance of
+// the drafts it makes (layout: this header in the first 256 bytes, then
+// each MASK row's (max, sum) [B][K] double2 (greedy: max and argmax), the
+// drafts' logits [B][K] float, the drafts [B][K] int32, each region
+// 256-byte aligned).
+struct MaskStatsHeader {
+  uint32_t magic;
+  uint32_t c2_bits;  // log2(e)/T as float32 bits (0 when greedy)
+  int32_t B, K, V, nsub;
+};
+constexpr uint32_t kMaskStatsMagic = 0x1D15A75Bu;
+struct MaskStatsLayout {
+  size_t off_st, off_dlog, off_tok, total;
+};
+MaskStatsLayout mask_stats_layout(const idlm_isd_dims& d);
 
 // Attention sizes derived from the dims.
 struct AttnPlan {
@@ -85,7 +108,7 @@ int32_t launch_paged_attn(const idlm_isd_dims& d, const Plan& p, const void* q, 
 int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
                       const int32_t* drafts, uint64_t seed, float T, int32_t* out_tokens,
                       int32_t* out_len, double* out_debug, char* ws, hipStream_t s,
-                      int32_t* status = nullptr);
+                      int32_t* status = nullptr, const void* mstats = nullptr);
 
 // Work-groups of the acceptance's launches (stats, decide + sums, select),
 // the largest of the three.  Host only; shared by validation and launch.
@@ -104,9 +127,11 @@ int32_t launch_gated_lora(const idlm_isd_lora_dims& L, const float* y_base, cons
                           const void* lora_a, const void* lora_b, float scale, void* y_out,
                           char* ws, hipStream_t s);
 
+// mstats (may be null): where to record the MASK-row statistics for the
+// next acceptance (else the workspace holds them).
 int32_t launch_propose(const idlm_isd_dims& d, const Plan& p, const void* logits_next,
                        const int32_t* drafts, const int32_t* accept_len, uint64_t seed, float T,
-                       int32_t* next_drafts, char* ws, hipStream_t s);
+                       int32_t* next_drafts, char* ws, hipStream_t s, void* mstats = nullptr);
 
 int32_t launch_kv_append(const idlm_isd_dims& d, const Plan& p, const void* k_new,
                          const void* v_new, const int32_t* ctx_before, int32_t* ctx_after,

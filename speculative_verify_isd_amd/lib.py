@@ -42,6 +42,7 @@ ENTRY_POINTS = (
     "idlm_isd_validate",
     "idlm_isd_workspace_init",
     "idlm_isd_paged_attn",
+    "idlm_isd_mask_stats_bytes",
     "idlm_isd_accept",
     "idlm_isd_accept_probs",
     "idlm_isd_accept_noalloc",
@@ -103,11 +104,12 @@ def load():
         "idlm_isd_validate": (i32, [D, f32]),
         "idlm_isd_workspace_init": (i32, [P, sz, P]),
         "idlm_isd_paged_attn": (i32, [D, P, P, P, P, P, P, sz, P]),
-        "idlm_isd_accept": (i32, [D, P, P, P, u64, f32, P, P, P, P, sz, P]),
+        "idlm_isd_accept": (i32, [D, P, P, P, u64, f32, P, P, P, P, P, sz, P]),
+        "idlm_isd_mask_stats_bytes": (sz, [D]),
         "idlm_isd_accept_probs": (i32, [D, P, P, f32, P, sz, P, P, P, P]),
-        "idlm_isd_accept_noalloc": (i32, [D, P, P, P, u64, f32, P, P, P, P, P]),
-        "idlm_isd_step": (i32, [D, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, sz, P]),
-        "idlm_isd_propose": (i32, [D, P, P, P, u64, f32, P, P, sz, P]),
+        "idlm_isd_accept_noalloc": (i32, [D, P, P, P, u64, f32, P, P, P, P, P, P]),
+        "idlm_isd_step": (i32, [D, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, P, sz, P]),
+        "idlm_isd_propose": (i32, [D, P, P, P, u64, f32, P, P, P, sz, P]),
         "idlm_isd_lora_workspace_bytes": (sz, [ctypes.POINTER(LoraDims)]),
         "idlm_isd_gated_lora": (i32, [ctypes.POINTER(LoraDims), P, P, P, P, f32, P, P, sz, P]),
         "idlm_isd_kv_append": (i32, [D, P, P, P, P, P, P, P, P, P, sz, P]),
@@ -245,8 +247,28 @@ def idlm_isd_paged_attn(dims, q, kv_pages, page_table, ctx_lens, attn_out, ws):
         ws.numel(), _stream()), "idlm_isd_paged_attn")
 
 
+def idlm_isd_mask_stats_bytes(dims):
+    return int(load().idlm_isd_mask_stats_bytes(ctypes.byref(dims)))
+
+
+def alloc_mask_stats(dims, device="cuda"):
+    """A (256-byte aligned) MASK-row statistics record for ``dims``."""
+    torch = _torch()
+    n = idlm_isd_mask_stats_bytes(dims)
+    if n == 0:
+        raise IdlmError(2, "idlm_isd_mask_stats_bytes")
+    m = torch.zeros(n + 256, dtype=torch.uint8, device=device)
+    off = (-m.data_ptr()) % 256
+    return m[off:off + n]
+
+
+def _mstats(mask_stats, dims):
+    return _ptr(mask_stats, (_torch().uint8,), "mask_stats", allow_none=True,
+                numel=idlm_isd_mask_stats_bytes(dims) if mask_stats is not None else None)
+
+
 def idlm_isd_accept(dims, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
-                    out_accept_len, out_debug, ws):
+                    out_accept_len, out_debug, ws, mask_stats=None):
     ft = _fdt(dims.logits_dtype)
     torch = _torch()
     n = _sizes(dims)
@@ -258,11 +280,12 @@ def idlm_isd_accept(dims, logits_clean, logits_mask, draft_tokens, seed, T, out_
         _ptr(out_tokens, _i32(), "out_tokens", numel=n["tokens"]),
         _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
         _ptr(out_debug, (torch.float64,), "out_debug", allow_none=True, numel=n["debug"]),
+        _mstats(mask_stats, dims),
         _ptr(ws, (torch.uint8,), "workspace"), ws.numel(), _stream()), "idlm_isd_accept")
 
 
 def idlm_isd_accept_noalloc(dims, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
-                            out_accept_len, out_debug=None, out_status=None):
+                            out_accept_len, out_debug=None, out_status=None, mask_stats=None):
     ft = _fdt(dims.logits_dtype)
     torch = _torch()
     n = _sizes(dims)
@@ -274,6 +297,7 @@ def idlm_isd_accept_noalloc(dims, logits_clean, logits_mask, draft_tokens, seed,
         _ptr(out_tokens, _i32(), "out_tokens", numel=n["tokens"]),
         _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
         _ptr(out_debug, (torch.float64,), "out_debug", allow_none=True, numel=n["debug"]),
+        _mstats(mask_stats, dims),
         _ptr(out_status, _i32(), "out_status", allow_none=True, numel=1), _stream()),
         "idlm_isd_accept_noalloc")
 
@@ -295,7 +319,8 @@ def idlm_isd_accept_probs(dims, logits_clean, logits_mask, T, ws, out_p=None, ou
 
 
 def idlm_isd_step(dims, q, kv_pages, page_table, ctx_lens, logits_clean, logits_mask,
-                  draft_tokens, seed, N, T, out_tokens, out_accept_len, attn_out, ws):
+                  draft_tokens, seed, N, T, out_tokens, out_accept_len, attn_out, ws,
+                  mask_stats=None):
     fq = _fdt(dims.qkv_dtype)
     fl = _fdt(dims.logits_dtype)
     torch = _torch()
@@ -311,11 +336,12 @@ def idlm_isd_step(dims, q, kv_pages, page_table, ctx_lens, logits_clean, logits_
         ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), int(N), float(T),
         _ptr(out_tokens, _i32(), "out_tokens", numel=n["tokens"]),
         _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
-        _ptr(attn_out, fq, "attn_out", numel=n["q"]), _ptr(ws, (torch.uint8,), "workspace"),
-        ws.numel(), _stream()), "idlm_isd_step")
+        _ptr(attn_out, fq, "attn_out", numel=n["q"]), _mstats(mask_stats, dims),
+        _ptr(ws, (torch.uint8,), "workspace"), ws.numel(), _stream()), "idlm_isd_step")
 
 
-def idlm_isd_propose(dims, logits_next, draft_tokens, accept_len, seed, T, next_drafts, ws):
+def idlm_isd_propose(dims, logits_next, draft_tokens, accept_len, seed, T, next_drafts, ws,
+                     mask_stats=None):
     n = _sizes(dims)
     _check(load().idlm_isd_propose(
         ctypes.byref(dims),
@@ -324,6 +350,7 @@ def idlm_isd_propose(dims, logits_next, draft_tokens, accept_len, seed, T, next_
         _ptr(accept_len, _i32(), "accept_len", numel=n["B"] if dims.N > 1 else 0),  # N = 1: no-op
         ctypes.c_uint64(int(seed) & (2**64 - 1)), ctypes.c_float(float(T)),
         _ptr(next_drafts, _i32(), "next_drafts", numel=n["drafts"]),
+        _mstats(mask_stats, dims),
         _ptr(ws, (_torch().uint8,), "workspace"),
         ctypes.c_size_t(ws.numel()), _stream()),
         "idlm_isd_propose")
@@ -436,10 +463,11 @@ class DeviceStep:
         idlm_isd_paged_attn(self.dims, self.q, self.kv, self.page_table, self.ctx_lens, self.out,
                             self.ws)
 
-    def accept(self, seed=None, T=None, debug=True):
-        idlm_isd_accept(self.dims, self.lc, self.lm, self.drafts,
+    def accept(self, seed=None, T=None, debug=True, drafts=None, mask_stats=None):
+        idlm_isd_accept(self.dims, self.lc, self.lm, self.drafts if drafts is None else drafts,
                         self.w.seed if seed is None else seed, self.w.T if T is None else T,
-                        self.tokens, self.lens, self.debug if debug else None, self.ws)
+                        self.tokens, self.lens, self.debug if debug else None, self.ws,
+                        mask_stats=mask_stats)
 
     def probs(self, T=None):
         """(p [B][N][V], q [B][K][V], sub-chunk weights [B][ceil(V/2048)]) as
@@ -454,10 +482,12 @@ class DeviceStep:
                               p, q if w.N > 1 else None, sw)
         return p, q, sw
 
-    def step(self, seed=None, T=None):
+    def step(self, seed=None, T=None, drafts=None, mask_stats=None):
         idlm_isd_step(self.dims, self.q, self.kv, self.page_table, self.ctx_lens, self.lc, self.lm,
-                      self.drafts, self.w.seed if seed is None else seed, self.w.N,
-                      self.w.T if T is None else T, self.tokens, self.lens, self.out, self.ws)
+                      self.drafts if drafts is None else drafts,
+                      self.w.seed if seed is None else seed, self.w.N,
+                      self.w.T if T is None else T, self.tokens, self.lens, self.out, self.ws,
+                      mask_stats=mask_stats)
 
     def out_f64(self):
         return self.out.to(_torch().float64).cpu().numpy()

@@ -62,17 +62,19 @@ int main(void) {
   EXPECT(idlm_isd_validate(NULL, 1.0f), IDLM_ERR_NULL);
   EXPECT(idlm_isd_workspace_bytes(NULL), 0);
   EXPECT(idlm_isd_workspace_state_bytes(NULL), 0);
+  EXPECT(idlm_isd_mask_stats_bytes(NULL), 0);
+  EXPECT(idlm_isd_mask_stats_bytes(&d) > 256, 1);
 
   /* NULL dims everywhere */
   EXPECT(idlm_isd_paged_attn(NULL, fake, fake, fake, fake, fake, fake, n, NULL), IDLM_ERR_NULL);
-  EXPECT(idlm_isd_accept(NULL, fake, fake, fake, 1, 1.0f, fake, fake, NULL, fake, n, NULL),
+  EXPECT(idlm_isd_accept(NULL, fake, fake, fake, 1, 1.0f, fake, fake, NULL, NULL, fake, n, NULL),
          IDLM_ERR_NULL);
   EXPECT(idlm_isd_accept_probs(NULL, fake, fake, 1.0f, fake, n, fake, fake, fake, NULL),
          IDLM_ERR_NULL);
   EXPECT(idlm_isd_step(NULL, fake, fake, fake, fake, fake, fake, fake, 1, 4, 1.0f, fake, fake,
-                       fake, fake, n, NULL),
+                       fake, NULL, fake, n, NULL),
          IDLM_ERR_NULL);
-  EXPECT(idlm_isd_propose(NULL, fake, fake, fake, 1, 1.0f, fake, fake, n, NULL), IDLM_ERR_NULL);
+  EXPECT(idlm_isd_propose(NULL, fake, fake, fake, 1, 1.0f, fake, NULL, fake, n, NULL), IDLM_ERR_NULL);
   EXPECT(idlm_isd_kv_append(NULL, fake, fake, fake, fake, fake, fake, fake, fake, fake, n, NULL),
          IDLM_ERR_NULL);
   EXPECT(idlm_isd_kv_rollback(NULL, fake, fake, fake, fake, fake, fake, fake, n, NULL),
@@ -85,25 +87,25 @@ int main(void) {
   EXPECT(idlm_isd_paged_attn(&d, fake, fake, fake, fake, fake, NULL, n, NULL), IDLM_ERR_NULL);
   EXPECT(idlm_isd_paged_attn(&d, fake, fake, fake, fake, fake, fake, n - 256, NULL),
          IDLM_ERR_WORKSPACE);
-  EXPECT(idlm_isd_accept(&d, fake, fake, fake, 1, 1.0f, fake, fake, NULL, misaligned, n, NULL),
+  EXPECT(idlm_isd_accept(&d, fake, fake, fake, 1, 1.0f, fake, fake, NULL, NULL, misaligned, n, NULL),
          IDLM_ERR_WORKSPACE);
   EXPECT(idlm_isd_accept_probs(&d, fake, fake, 1.0f, fake, n - 256, fake, fake, fake, NULL),
          IDLM_ERR_WORKSPACE);
-  EXPECT(idlm_isd_propose(&d, fake, fake, fake, 1, 1.0f, fake, misaligned, n, NULL),
+  EXPECT(idlm_isd_propose(&d, fake, fake, fake, 1, 1.0f, fake, NULL, misaligned, n, NULL),
          IDLM_ERR_WORKSPACE);
   EXPECT(idlm_isd_workspace_init(misaligned, 1024, NULL), IDLM_ERR_WORKSPACE);
 
   /* temperature and required pointers */
-  EXPECT(idlm_isd_accept(&d, fake, fake, fake, 1, -1.0f, fake, fake, NULL, fake, n, NULL),
+  EXPECT(idlm_isd_accept(&d, fake, fake, fake, 1, -1.0f, fake, fake, NULL, NULL, fake, n, NULL),
          IDLM_ERR_TEMPERATURE);
-  EXPECT(idlm_isd_accept(&d, NULL, fake, fake, 1, 1.0f, fake, fake, NULL, fake, n, NULL),
+  EXPECT(idlm_isd_accept(&d, NULL, fake, fake, 1, 1.0f, fake, fake, NULL, NULL, fake, n, NULL),
          IDLM_ERR_NULL);
   EXPECT(idlm_isd_accept_probs(&d, fake, fake, NAN, fake, n, fake, fake, fake, NULL),
          IDLM_ERR_TEMPERATURE);
-  EXPECT(idlm_isd_propose(&d, fake, fake, fake, 1, INFINITY, fake, fake, n, NULL),
+  EXPECT(idlm_isd_propose(&d, fake, fake, fake, 1, INFINITY, fake, NULL, fake, n, NULL),
          IDLM_ERR_TEMPERATURE);
   EXPECT(idlm_isd_step(&d, fake, fake, fake, fake, fake, fake, fake, 1, 3, 1.0f, fake, fake,
-                       fake, fake, n, NULL),
+                       fake, NULL, fake, n, NULL),
          IDLM_ERR_DIMS); /* N repeated must match */
 
   /* B = 0 is a no-op that touches nothing */
@@ -111,9 +113,9 @@ int main(void) {
   z.B = 0;
   const size_t nz = idlm_isd_workspace_bytes(&z);
   EXPECT(idlm_isd_step(&z, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, 4, 1.0f, NULL, NULL, NULL,
-                       fake, nz, NULL),
+                       NULL, fake, nz, NULL),
          IDLM_OK);
-  EXPECT(idlm_isd_accept(&z, NULL, NULL, NULL, 1, 1.0f, NULL, NULL, NULL, fake, nz, NULL),
+  EXPECT(idlm_isd_accept(&z, NULL, NULL, NULL, 1, 1.0f, NULL, NULL, NULL, NULL, fake, nz, NULL),
          IDLM_OK);
 
   /* gated LoRA */
@@ -156,6 +158,7 @@ int main(void) {
            1);
     EXPECT((vd == IDLM_OK) == (w > 0), 1);
     EXPECT((vd == IDLM_OK) == (s > 0 && s < w), 1);
+    EXPECT((vd == IDLM_OK) == (idlm_isd_mask_stats_bytes(&r) >= 256), 1);
     idlm_isd_lora_dims l = {pick(1 << 12), pick(17), pick(1 << 16), pick(1 << 16), pick(300)};
     (void)idlm_isd_lora_workspace_bytes(&l);
   }

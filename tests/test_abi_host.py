@@ -96,14 +96,17 @@ def test_entry_points_validate_before_launch(so):
     assert so.idlm_isd_paged_attn(ctypes.byref(d), fake, fake, fake, fake, fake, fake, n - 256,
                                   None) == 5
     misaligned = ctypes.c_void_p((1 << 20) + 8)
-    assert so.idlm_isd_accept(ctypes.byref(d), fake, fake, fake, 1, 1.0, fake, fake, None,
+    assert so.idlm_isd_accept(ctypes.byref(d), fake, fake, fake, 1, 1.0, fake, fake, None, None,
                               misaligned, n, None) == 5
-    assert so.idlm_isd_accept(ctypes.byref(d), fake, fake, fake, 1, -1.0, fake, fake, None,
+    assert so.idlm_isd_accept(ctypes.byref(d), fake, fake, fake, 1, -1.0, fake, fake, None, None,
                               fake, n, None) == 4
-    assert so.idlm_isd_accept(ctypes.byref(d), None, fake, fake, 1, 1.0, fake, fake, None,
+    assert so.idlm_isd_accept(ctypes.byref(d), None, fake, fake, 1, 1.0, fake, fake, None, None,
                               fake, n, None) == 1
+    # a misaligned MASK-row statistics record
+    assert so.idlm_isd_accept(ctypes.byref(d), fake, fake, fake, 1, 1.0, fake, fake, None,
+                              misaligned, fake, n, None) == 5
     assert so.idlm_isd_step(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, 1, 3, 1.0,
-                            fake, fake, fake, fake, n, None) == 2  # N repeated must match
+                            fake, fake, fake, None, fake, n, None) == 2  # N repeated must match
     assert so.idlm_isd_read_status(None, None, None) == 1
     assert so.idlm_isd_workspace_init(misaligned, 1024, None) == 5
 
@@ -113,7 +116,7 @@ def test_empty_batch_is_a_no_op(so):
     n = L.idlm_isd_workspace_bytes(d)
     fake = ctypes.c_void_p(1 << 20)
     assert so.idlm_isd_step(ctypes.byref(d), None, None, None, None, None, None, None, 1, 4, 1.0,
-                            None, None, None, fake, n, None) == 0
+                            None, None, None, None, fake, n, None) == 0
 
 
 def test_strerror(so):
@@ -319,11 +322,11 @@ def test_accept_noalloc_validates_before_launch(so):
     f = ctypes.c_float
     d = good()
     assert so.idlm_isd_accept_noalloc(None, fake, fake, fake, 1, f(1.0), fake, fake, None, None,
-                                      None) == 1
+                                      None, None) == 1
     assert so.idlm_isd_accept_noalloc(ctypes.byref(d), fake, fake, fake, 1, f(-1.0), fake, fake,
-                                      None, None, None) == 4
+                                      None, None, None, None) == 4
     assert so.idlm_isd_accept_noalloc(ctypes.byref(d), None, fake, fake, 1, f(1.0), fake, fake,
-                                      None, None, None) == 1
+                                      None, None, None, None) == 1
     # The scratch need stated in the header: 256 bytes plus seven regions,
     # each rounded up to 256 bytes.  Sizes over 8 MiB are refused (8) before
     # anything is looked up; sizes within it reach the pointer checks (1).
@@ -338,8 +341,23 @@ def test_accept_noalloc_validates_before_launch(so):
         big = good(B=B)
         assert L.idlm_isd_validate(big, 1.0) == 0
         assert so.idlm_isd_accept_noalloc(ctypes.byref(big), None, fake, fake, 1, f(1.0), fake,
-                                          fake, None, None, None) == code
+                                          fake, None, None, None, None) == code
     assert L.strerror(8) != "unknown status"
     z = good(B=0)
     assert so.idlm_isd_accept_noalloc(ctypes.byref(z), None, None, None, 1, f(1.0), None, None,
-                                      None, None, None) == 0
+                                      None, None, None, None) == 0
+
+
+def test_mask_stats_bytes(so):
+    # header (256) + each MASK row's (max, sum) [B][K] + logits and drafts [B][K]
+    d = good()
+    K = 3
+    r = lambda x: -(-x // 256) * 256
+    assert L.idlm_isd_mask_stats_bytes(d) == 256 + r(64 * K * 16) + r(64 * K * 4) * 2
+    assert L.idlm_isd_mask_stats_bytes(good(N=1)) == 256
+    assert L.idlm_isd_mask_stats_bytes(good(D=96)) == 0
+    assert so.idlm_isd_mask_stats_bytes(None) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    n = L.idlm_isd_workspace_bytes(d)
+    assert so.idlm_isd_propose(ctypes.byref(d), fake, fake, fake, 1, ctypes.c_float(1.0), fake,
+                               ctypes.c_void_p((1 << 20) + 64), fake, n, None) == 5

@@ -146,3 +146,69 @@ def test_decode_loop_reaches_closed_form(torch_cuda):
     print(f"[loop] GPU decode loop: {B} sequences x {steps} forwards, tokens per forward "
           f"{tpf:.4f} vs closed form {want:.4f}", flush=True)
     assert abs(tpf - want) < 0.02
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_loop_with_mask_stats_matches_plain_acceptance(torch_cuda, T):
+    """A decode loop over changing logits (clean rows of step t = MASK rows of
+    step t-1 plus N(0, 0.5^2), bonus and new MASK rows fresh): the proposals
+    record their MASK rows' statistics, and the acceptance of their drafts
+    with that record (only the N clean rows reduced) gives the same tokens
+    and lengths as without it, and as the oracle."""
+    torch = torch_cuda
+    from speculative_verify_isd_amd import lib as L
+    from oracle.accept import isd_accept as oracle_accept_batch
+
+    B, N, V, steps, sigma = 16, 4, 151936, 6, 0.5
+    K = N - 1
+    rng = np.random.default_rng(77 + int(T))
+    mask = [rng.normal(0, 3, (B, K, V)).astype(np.float32)]
+    clean = [None]
+    for t in range(1, steps + 1):
+        c = np.empty((B, N, V), dtype=np.float32)
+        c[:, :K] = mask[t - 1] + rng.normal(0, sigma, (B, K, V)).astype(np.float32)
+        c[:, K] = rng.normal(0, 3, (B, V)).astype(np.float32)
+        clean.append(W.f32_to_bf16_bits(c))
+        mask.append(rng.normal(0, 3, (B, K, V)).astype(np.float32))
+    mask = [W.f32_to_bf16_bits(m) for m in mask]
+    dims = L.make_dims(B, N, 8, 2, 64, V, 4, 4, "bf16", "bf16")
+    ws = L.alloc_workspace(dims)
+    ms = L.alloc_mask_stats(dims)
+    dev = lambda a: _dev(torch, a, "bf16")
+    drafts = torch.full((B, K), -1, dtype=torch.int32, device="cuda")
+    lens = torch.ones(B, dtype=torch.int32, device="cuda")
+    nxt = torch.empty_like(drafts)
+    toks_a, toks_b = (torch.empty((B, N), dtype=torch.int32, device="cuda") for _ in range(2))
+    lens_a, lens_b = (torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(2))
+    verified = 0
+    for t in range(1, steps + 1):
+        d_prev, d_clean = dev(mask[t - 1]), dev(clean[t])
+        L.idlm_isd_propose(dims, d_prev, drafts, lens, 500 + t, T, nxt, ws, mask_stats=ms)
+        L.idlm_isd_accept(dims, d_clean, d_prev, nxt, t, T, toks_a, lens_a, None, ws)
+        L.idlm_isd_accept(dims, d_clean, d_prev, nxt, t, T, toks_b, lens_b, None, ws,
+                          mask_stats=ms)
+        torch.cuda.synchronize()
+        assert L.idlm_isd_read_status(ws) == 0
+        ta, tb = toks_a.cpu().numpy(), toks_b.cpu().numpy()
+        la, lb = lens_a.cpu().numpy(), lens_b.cpu().numpy()
+        dr = nxt.cpu().numpy()
+        assert np.array_equal(la, lb) and np.array_equal(ta, tb), t
+        o_tok, o_len, _ = oracle_accept_batch(clean[t], mask[t - 1], dr, t, float(np.float32(T)),
+                                              dtype="bf16")
+        assert np.array_equal(o_len, la) and np.array_equal(o_tok, ta), t
+        verified += int((dr[:, 0] >= 0).sum())
+        drafts.copy_(nxt)
+        lens.copy_(lens_a)
+    print(f"[loop] T={T}: {steps} steps, {verified} verifying sequence-steps, mask-stats "
+          f"acceptance identical to the plain one and to the oracle", flush=True)
+    assert verified >= B  # the record was actually used
+
+    # A record made at another temperature, or for other drafts, is flagged.
+    d_prev = dev(mask[steps - 1])
+    L.idlm_isd_propose(dims, d_prev, drafts, lens, 900, 0.7 if T else 1.0, nxt, ws, mask_stats=ms)
+    L.idlm_isd_accept(dims, dev(clean[steps]), d_prev, nxt, 1, T, toks_b, lens_b, None, ws,
+                      mask_stats=ms)
+    torch.cuda.synchronize()
+    flagged = L.idlm_isd_read_status(ws)
+    verifying = bool((nxt[:, 0] >= 0).any().item())
+    assert flagged == (7 if verifying else 0)
