@@ -15,8 +15,10 @@ namespace {
 // from the caller's stream and joined back to it with events: the two stages
 // read different inputs and write disjoint workspace regions (the sticky
 // status word is set with atomic ORs), and run side by side on the chip.
-// One set per device, created once; enqueueing a fork holds the mutex so the
-// event record / wait pairs of concurrent host threads do not interleave.
+// One set per device, created once; enqueueing a fork holds that device's
+// mutex so the event record / wait pairs of concurrent host threads on one
+// device do not interleave (steps on different devices do not wait for each
+// other).
 struct ForkSet {
   hipStream_t aux = nullptr;
   hipEvent_t start = nullptr, done = nullptr;
@@ -29,13 +31,18 @@ ForkSet g_fork[kMaxDevices];
 // logits (B * R * V).  Measured per step: B = 16, V = 151936 (17M logits)
 // 87.9 -> 81.2 us; C = 64 (68M) 414 -> 394 us; B = 1 (1M) 38.7 -> 66.8 us.
 constexpr int64_t kForkMinLogits = (int64_t)1 << 23;
-std::mutex g_fork_mu;
+std::mutex g_fork_mu[kMaxDevices];
 
-// The current device's set (created on first use), or nullptr when it cannot
-// be had; the caller holds g_fork_mu.
-ForkSet* fork_set() {
+// The current device, or -1 when it cannot be had or lies past the sets.
+int fork_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  return dev;
+}
+
+// Device dev's set (created on first use), or nullptr when it cannot be had;
+// the caller holds g_fork_mu[dev].
+ForkSet* fork_set(int dev) {
   ForkSet& f = g_fork[dev];
   if (f.ok) return &f;
   if (!f.aux && hipStreamCreateWithFlags(&f.aux, hipStreamNonBlocking) != hipSuccess) {
@@ -255,9 +262,10 @@ int32_t idlm_isd_validate(const idlm_isd_dims* d, float T) {
 int32_t idlm_isd_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
   if (!workspace) return IDLM_ERR_NULL;
   if (((uintptr_t)workspace & 255) != 0) return IDLM_ERR_WORKSPACE;
-  {  // the step's second stream and events, made here outside any capture
-    std::lock_guard<std::mutex> g(g_fork_mu);
-    fork_set();
+  const int dev = fork_device();
+  if (dev >= 0) {  // the step's second stream and events, made here outside any capture
+    std::lock_guard<std::mutex> g(g_fork_mu[dev]);
+    fork_set(dev);
   }
   if (ws_bytes == 0) return IDLM_OK;
   return launch_fill_zero(workspace, ws_bytes, (hipStream_t)stream);
@@ -365,9 +373,13 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
   if (!logits_clean || !out_tokens || !out_accept_len) return IDLM_ERR_NULL;
   if (d->N > 1 && (!logits_mask || !draft_tokens)) return IDLM_ERR_NULL;
   hipStream_t s = (hipStream_t)stream;
-  std::lock_guard<std::mutex> g(g_fork_mu);
   const int64_t logits = (int64_t)d->B * (2 * d->N - 1) * d->V;
-  ForkSet* f = logits >= kForkMinLogits ? fork_set() : nullptr;
+  const int dev = logits >= kForkMinLogits ? fork_device() : -1;
+  // Held for the whole enqueue: the fork's events are shared by the
+  // device's steps.
+  std::unique_lock<std::mutex> g;
+  if (dev >= 0) g = std::unique_lock<std::mutex>(g_fork_mu[dev]);
+  ForkSet* f = dev >= 0 ? fork_set(dev) : nullptr;
   hipStream_t sa = s;  // the acceptance's stream: the fork, or `stream` itself without one
   if (f) {
     if (hipEventRecord(f->start, s) != hipSuccess) return IDLM_ERR_HIP;

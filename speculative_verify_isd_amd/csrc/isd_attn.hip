@@ -43,6 +43,8 @@
 //   (the query fragments live in LDS to leave registers to the ring); page
 //   ids are wave-uniform loads.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <math.h>
 
 #include "isd_internal.hpp"
@@ -959,12 +961,17 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 }
 
 // Work-groups the streaming kernel keeps resident on this device (queried
-// once per device): every CU times the kernel's occupancy.
+// once per device, cached in an atomic so concurrent first calls from
+// several host threads are well defined; devices past the cache are queried
+// every time): every CU times the kernel's occupancy.
 template <int D, int WR, int RB>
 int stream_grid(int device) {
-  static int cached[64] = {0};
-  if (device < 0 || device >= 64) device = 0;
-  if (cached[device]) return cached[device];
+  static std::atomic<int> cached[64];
+  const bool cache = device >= 0 && device < 64;
+  if (cache) {
+    const int g = cached[device].load(std::memory_order_relaxed);
+    if (g) return g;
+  }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
       cus <= 0)
@@ -976,7 +983,7 @@ int stream_grid(int device) {
   int g = cus * per_cu;
   const int cap = kMaxWaves / 4;
   if (g > cap) g = cap;
-  cached[device] = g;
+  if (cache) cached[device].store(g, std::memory_order_relaxed);
   return g;
 }
 
