@@ -242,15 +242,16 @@ def time_propose(ds, w, K):
 
 
 def time_loop(ds, w, K):
-    """The decode loop: each iteration is one step (attention beside the
-    acceptance) whose acceptance takes the MASK-row statistics the previous
-    proposal recorded, then the proposals for the next iteration, which
-    record theirs (two records, alternating).  The workload's MASK rows stand
-    in for every forward's (same shape); each iteration's drafts are the
-    previous proposals, so sequences whose drafts were all kept keep
-    verifying and the others start fresh.  Also the acceptance alone with
-    and without the record on the same drafts (attention call before each,
-    as for the other per-call times)."""
+    """The decode loop at this workload's shapes: each iteration verifies the
+    previous proposals (with the MASK-row statistics they recorded) and
+    proposes the next drafts.  The workload's MASK rows stand in for every
+    forward's (same shape); sequences whose drafts were all kept keep
+    verifying, the others start fresh.  Timed two ways: one
+    idlm_isd_loop_step per iteration (proposals beside the attention, one
+    record rewritten in place), and idlm_isd_step then idlm_isd_propose (two
+    records, alternating).  Also the acceptance alone with and without the
+    record on the same drafts (attention call before each, as for the other
+    per-call times)."""
     import torch
 
     from speculative_verify_isd_amd import lib as L
@@ -264,60 +265,76 @@ def time_loop(ds, w, K):
     lens = torch.ones(w.B, dtype=torch.int32, device="cuda")
     # prime: proposals from a fresh start record the first statistics
     L.idlm_isd_propose(ds.dims, ds.lm, d[0], lens, 11, w.T, d[1], ds.ws, mask_stats=ms[1])
+    L.idlm_isd_propose(ds.dims, ds.lm, d[0], lens, 11, w.T, d[1], ds.ws, mask_stats=ms[0])
     cur = 1
 
-    def iteration(k):
+    def fused(k):
+        nonlocal cur
+        L.idlm_isd_loop_step(ds.dims, ds.q, ds.kv, ds.page_table, ds.ctx_lens, ds.lc, ds.lm,
+                             d[cur], ms[0], ds.lm, 100 + k, w.N, w.T, ds.tokens, ds.lens, ds.out,
+                             d[1 - cur], ms[0], ds.ws)
+        cur = 1 - cur
+
+    def separate(k):
         nonlocal cur
         ds.step(seed=100 + k, drafts=d[cur], mask_stats=ms[cur])
-        L.idlm_isd_propose(ds.dims, ds.lm, d[cur], ds.lens, 200 + k, w.T, d[1 - cur], ds.ws,
+        L.idlm_isd_propose(ds.dims, ds.lm, d[cur], ds.lens, 100 + k, w.T, d[1 - cur], ds.ws,
                            mask_stats=ms[1 - cur])
         cur = 1 - cur
 
-    for k in range(5):
-        iteration(k)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for k in range(K):
-        iteration(k)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_loop = e0.elapsed_time(e1) / K
-    # committed tokens of K more iterations, counted outside the timed region
+    out = {}
+    for name, it in (("separate", separate), ("loop_step", fused)):
+        if name == "loop_step":  # the shared record must describe d[cur]
+            L.idlm_isd_propose(ds.dims, ds.lm, d[0], lens, 12, w.T, d[1], ds.ws, mask_stats=ms[0])
+            cur = 1
+        for k in range(5):
+            it(k)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(K):
+            it(k)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) / K
+    # committed tokens of K more loop steps, counted outside the timed regions
     committed = torch.zeros(1, dtype=torch.int64, device="cuda")
     for k in range(K):
-        iteration(K + k)
+        fused(K + k)
         committed += ds.lens.sum()
     torch.cuda.synchronize()
     assert L.idlm_isd_read_status(ds.ws) == 0
     tok = float(committed.item())
 
     # the acceptance alone, with and without the record, on the same drafts
+    L.idlm_isd_propose(ds.dims, ds.lm, d[0], lens, 13, w.T, d[1], ds.ws, mask_stats=ms[1])
     times = {}
-    for name, rec in (("with", ms[cur]), ("without", None)):
+    for name, rec in (("with", ms[1]), ("without", None)):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
         for k in range(K + 3):
             ds.attn()
             e = ev[k - 3] if k >= 3 else None
             if e:
                 e[0].record()
-            ds.accept(seed=300, debug=False, drafts=d[cur], mask_stats=rec)
+            ds.accept(seed=300, debug=False, drafts=d[1], mask_stats=rec)
             if e:
                 e[1].record()
         torch.cuda.synchronize()
         times[name] = float(np.mean([x[0].elapsed_time(x[1]) for x in ev])) * 1e3
     assert L.idlm_isd_read_status(ds.ws) == 0
     lens_np = ds.lens.cpu().numpy()
-    kp = (d[cur].cpu().numpy() >= 0).sum(axis=1)
+    kp = (d[1].cpu().numpy() >= 0).sum(axis=1)
     resid = int(((lens_np - 1) < kp).sum())
     ds.accept(debug=False)  # leave the workload's own outputs in ds (the headline reads them)
     torch.cuda.synchronize()
     es = 2 if w.logits_dtype == "bf16" else 4
     nbytes = (w.B * w.N + 2 * resid + (w.B - resid)) * w.V * es + w.B * (w.N + 1) * 4
+    ms_loop = out["loop_step"]
     return {"loop": {"ms_per_step": ms_loop, "steps_per_s": 1000.0 / ms_loop,
                      "committed_tok_per_s": tok / K * 1000.0 / ms_loop,
                      "mean_accept_len": tok / (K * w.B),
+                     "ms_per_step_step_then_propose": out["separate"],
                      "accept_with_mask_stats_us": times["with"],
                      "accept_without_mask_stats_us": times["without"],
                      "accept_with_mask_stats_algorithmic_bytes": nbytes,

@@ -20,7 +20,10 @@
  *      "Inference & ISD"; GeekNews summary, section "Inference & ISD").
  *   3. idlm_isd_step: 1 and 2 side by side (they are independent).
  *   4. idlm_isd_propose: the next step's drafts from this forward's MASK
- *      rows, or a fresh step after a rejection.
+ *      rows, or a fresh step after a rejection; it can record the MASK
+ *      rows' statistics, which the next acceptance then does not recompute.
+ *      idlm_isd_loop_step: 3 and 4 in one call, the proposals beside the
+ *      attention.
  *   5. idlm_isd_gated_lora: R-ISD's adapter on MASK rows after the base
  *      projection (verify rows untouched).
  *   6. idlm_isd_kv_append / idlm_isd_kv_rollback: the cache writes around a
@@ -267,6 +270,30 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
                       const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
                       int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
                       const void* mask_stats, void* workspace, size_t ws_bytes, void* stream);
+
+/* One step of the decode loop: idlm_isd_step, then, on the acceptance's
+ * stream (beside the attention when the step forks), idlm_isd_propose of the
+ * next step's drafts from this forward's MASK rows:
+ *   logits_mask, draft_tokens, mask_stats   as for idlm_isd_step (the
+ *                  previous forward's MASK rows, the drafts made from them,
+ *                  and their record or NULL)
+ *   logits_next    [device] [B][K][V]: this forward's MASK rows
+ *   next_drafts    [device] int32 [B][K], written (as idlm_isd_propose)
+ *   mask_stats_next [device] or NULL, written: the record of next_drafts;
+ *                  may be the mask_stats buffer itself (the proposals run
+ *                  after the acceptance has read it)
+ * The proposals use the step's seed (their counters, (i, 1, 0, 0), are
+ * apart from the acceptance's) and T.  Results equal idlm_isd_step followed
+ * by idlm_isd_propose(d, logits_next, draft_tokens, out_accept_len, seed, T,
+ * next_drafts, mask_stats_next, ...). */
+int32_t idlm_isd_loop_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
+                           const int32_t* page_table, const int32_t* ctx_lens,
+                           const void* logits_clean, const void* logits_mask,
+                           const int32_t* draft_tokens, const void* mask_stats,
+                           const void* logits_next, uint64_t seed, int32_t N, float T,
+                           int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
+                           int32_t* next_drafts, void* mask_stats_next, void* workspace,
+                           size_t ws_bytes, void* stream);
 
 /* Drafts for the next step.  MASK rows propose the next tokens from q
  * ("Introspective Diffusion Language Models", section "Inference & ISD").

@@ -1153,7 +1153,10 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x / a.K, i = blockIdx.x % a.K;
   if (!continues(a, b)) {
-    if (tid == 0) put_draft(a, b, i, -1);
+    if (tid == 0) {
+      put_draft(a, b, i, -1);
+      if (a.mrow) a.mrow[(size_t)b * a.K + i] = make_double2(0.0, 0.0);  // no draft: unused
+    }
     return;
   }
   const double2* st = a.st + ((size_t)b * a.K + i) * a.nsub;

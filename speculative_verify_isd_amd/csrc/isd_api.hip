@@ -354,12 +354,20 @@ int32_t idlm_isd_accept_probs(const idlm_isd_dims* d, const void* logits_clean,
                             out_q, out_subw, (hipStream_t)stream);
 }
 
-int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
-                      const int32_t* page_table, const int32_t* ctx_lens,
-                      const void* logits_clean, const void* logits_mask,
-                      const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
-                      int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
-                      const void* mask_stats, void* workspace, size_t ws_bytes, void* stream) {
+// The next step's proposals of a loop step (absent for idlm_isd_step).
+struct NextProposals {
+  const void* logits_next;
+  int32_t* next_drafts;
+  void* mask_stats_next;
+};
+
+static int32_t step_impl(const idlm_isd_dims* d, const void* q, const void* kv_pages,
+                         const int32_t* page_table, const int32_t* ctx_lens,
+                         const void* logits_clean, const void* logits_mask,
+                         const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
+                         int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
+                         const void* mask_stats, const NextProposals* np, void* workspace,
+                         size_t ws_bytes, void* stream) {
   int32_t r = check_dims(d);
   if (r != IDLM_OK) return r;
   if (N != d->N) return IDLM_ERR_DIMS;
@@ -372,6 +380,10 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
   if (!q || !kv_pages || !page_table || !ctx_lens || !attn_out) return IDLM_ERR_NULL;
   if (!logits_clean || !out_tokens || !out_accept_len) return IDLM_ERR_NULL;
   if (d->N > 1 && (!logits_mask || !draft_tokens)) return IDLM_ERR_NULL;
+  if (np) {
+    if (((uintptr_t)np->mask_stats_next & 255) != 0) return IDLM_ERR_WORKSPACE;
+    if (d->N > 1 && (!np->logits_next || !np->next_drafts)) return IDLM_ERR_NULL;
+  }
   hipStream_t s = (hipStream_t)stream;
   const int64_t logits = (int64_t)d->B * (2 * d->N - 1) * d->V;
   const int dev = logits >= kForkMinLogits ? fork_device() : -1;
@@ -390,12 +402,42 @@ int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_page
   if (r == IDLM_OK)
     r = launch_accept(*d, p, logits_clean, logits_mask, draft_tokens, seed, T, out_tokens,
                       out_accept_len, nullptr, (char*)workspace, sa, nullptr, mask_stats);
+  // The proposals follow the acceptance on its stream: they need its accept
+  // lengths, and a record they write may be the one it read.
+  if (r == IDLM_OK && np)
+    r = launch_propose(*d, p, np->logits_next, draft_tokens, out_accept_len, seed, T,
+                       np->next_drafts, (char*)workspace, sa, np->mask_stats_next);
   // Join the second stream back whatever happened above, so a failed call
   // never leaves it forked (a capture in progress stays joined).
   if (f && (hipEventRecord(f->done, f->aux) != hipSuccess ||
             hipStreamWaitEvent(s, f->done, 0) != hipSuccess) && r == IDLM_OK)
     r = IDLM_ERR_HIP;
   return r;
+}
+
+int32_t idlm_isd_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
+                      const int32_t* page_table, const int32_t* ctx_lens,
+                      const void* logits_clean, const void* logits_mask,
+                      const int32_t* draft_tokens, uint64_t seed, int32_t N, float T,
+                      int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
+                      const void* mask_stats, void* workspace, size_t ws_bytes, void* stream) {
+  return step_impl(d, q, kv_pages, page_table, ctx_lens, logits_clean, logits_mask, draft_tokens,
+                   seed, N, T, out_tokens, out_accept_len, attn_out, mask_stats, nullptr,
+                   workspace, ws_bytes, stream);
+}
+
+int32_t idlm_isd_loop_step(const idlm_isd_dims* d, const void* q, const void* kv_pages,
+                           const int32_t* page_table, const int32_t* ctx_lens,
+                           const void* logits_clean, const void* logits_mask,
+                           const int32_t* draft_tokens, const void* mask_stats,
+                           const void* logits_next, uint64_t seed, int32_t N, float T,
+                           int32_t* out_tokens, int32_t* out_accept_len, void* attn_out,
+                           int32_t* next_drafts, void* mask_stats_next, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  const NextProposals np{logits_next, next_drafts, mask_stats_next};
+  return step_impl(d, q, kv_pages, page_table, ctx_lens, logits_clean, logits_mask, draft_tokens,
+                   seed, N, T, out_tokens, out_accept_len, attn_out, mask_stats, &np,
+                   workspace, ws_bytes, stream);
 }
 
 int32_t idlm_isd_propose(const idlm_isd_dims* d, const void* logits_next,

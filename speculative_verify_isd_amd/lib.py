@@ -47,6 +47,7 @@ ENTRY_POINTS = (
     "idlm_isd_accept_probs",
     "idlm_isd_accept_noalloc",
     "idlm_isd_step",
+    "idlm_isd_loop_step",
     "idlm_isd_propose",
     "idlm_isd_lora_workspace_bytes",
     "idlm_isd_gated_lora",
@@ -109,6 +110,8 @@ def load():
         "idlm_isd_accept_probs": (i32, [D, P, P, f32, P, sz, P, P, P, P]),
         "idlm_isd_accept_noalloc": (i32, [D, P, P, P, u64, f32, P, P, P, P, P, P]),
         "idlm_isd_step": (i32, [D, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, P, sz, P]),
+        "idlm_isd_loop_step": (i32, [D, P, P, P, P, P, P, P, P, P, u64, i32, f32, P, P, P, P, P,
+                                     P, sz, P]),
         "idlm_isd_propose": (i32, [D, P, P, P, u64, f32, P, P, P, sz, P]),
         "idlm_isd_lora_workspace_bytes": (sz, [ctypes.POINTER(LoraDims)]),
         "idlm_isd_gated_lora": (i32, [ctypes.POINTER(LoraDims), P, P, P, P, f32, P, P, sz, P]),
@@ -338,6 +341,32 @@ def idlm_isd_step(dims, q, kv_pages, page_table, ctx_lens, logits_clean, logits_
         _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
         _ptr(attn_out, fq, "attn_out", numel=n["q"]), _mstats(mask_stats, dims),
         _ptr(ws, (torch.uint8,), "workspace"), ws.numel(), _stream()), "idlm_isd_step")
+
+
+def idlm_isd_loop_step(dims, q, kv_pages, page_table, ctx_lens, logits_clean, logits_mask,
+                       draft_tokens, mask_stats, logits_next, seed, N, T, out_tokens,
+                       out_accept_len, attn_out, next_drafts, mask_stats_next, ws):
+    fq = _fdt(dims.qkv_dtype)
+    fl = _fdt(dims.logits_dtype)
+    torch = _torch()
+    n = _sizes(dims)
+    _check(load().idlm_isd_loop_step(
+        ctypes.byref(dims), _ptr(q, fq, "q", numel=n["q"]),
+        _ptr(kv_pages, fq, "kv_pages", numel=n["kv"]),
+        _ptr(page_table, _i32(), "page_table", numel=n["page_table"]),
+        _ptr(ctx_lens, _i32(), "ctx_lens", numel=n["B"]),
+        _ptr(logits_clean, fl, "logits_clean", numel=n["clean"]),
+        _ptr(logits_mask, fl, "logits_mask", allow_none=True, numel=n["mask"]),
+        _ptr(draft_tokens, _i32(), "draft_tokens", allow_none=True, numel=n["drafts"]),
+        _mstats(mask_stats, dims),
+        _ptr(logits_next, fl, "logits_next", allow_none=True, numel=n["mask"]),
+        ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), int(N), float(T),
+        _ptr(out_tokens, _i32(), "out_tokens", numel=n["tokens"]),
+        _ptr(out_accept_len, _i32(), "out_accept_len", numel=n["B"]),
+        _ptr(attn_out, fq, "attn_out", numel=n["q"]),
+        _ptr(next_drafts, _i32(), "next_drafts", allow_none=True, numel=n["drafts"]),
+        _mstats(mask_stats_next, dims),
+        _ptr(ws, (torch.uint8,), "workspace"), ws.numel(), _stream()), "idlm_isd_loop_step")
 
 
 def idlm_isd_propose(dims, logits_next, draft_tokens, accept_len, seed, T, next_drafts, ws,

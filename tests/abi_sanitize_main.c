@@ -75,6 +75,12 @@ int main(void) {
                        fake, NULL, fake, n, NULL),
          IDLM_ERR_NULL);
   EXPECT(idlm_isd_propose(NULL, fake, fake, fake, 1, 1.0f, fake, NULL, fake, n, NULL), IDLM_ERR_NULL);
+  EXPECT(idlm_isd_loop_step(NULL, fake, fake, fake, fake, fake, fake, fake, NULL, fake, 1, 4, 1.0f,
+                            fake, fake, fake, fake, NULL, fake, n, NULL),
+         IDLM_ERR_NULL);
+  EXPECT(idlm_isd_loop_step(&d, fake, fake, fake, fake, fake, fake, fake, NULL, fake, 1, 4, 1.0f,
+                            fake, fake, fake, fake, misaligned, fake, n, NULL),
+         IDLM_ERR_WORKSPACE);
   EXPECT(idlm_isd_kv_append(NULL, fake, fake, fake, fake, fake, fake, fake, fake, fake, n, NULL),
          IDLM_ERR_NULL);
   EXPECT(idlm_isd_kv_rollback(NULL, fake, fake, fake, fake, fake, fake, fake, n, NULL),

@@ -348,6 +348,24 @@ def test_accept_noalloc_validates_before_launch(so):
                                       None, None, None, None) == 0
 
 
+def test_loop_step_validates_before_launch(so):
+    d = good()
+    n = L.idlm_isd_workspace_bytes(d)
+    fake = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 64)
+    f = ctypes.c_float(1.0)
+    args = lambda ms_next, nxt, ln: (fake, fake, fake, fake, fake, fake, fake, None, ln, 1, 4, f,
+                                     fake, fake, fake, nxt, ms_next, fake, n, None)
+    assert so.idlm_isd_loop_step(None, *args(None, fake, fake)) == 1
+    assert so.idlm_isd_loop_step(ctypes.byref(d), *args(mis, fake, fake)) == 5
+    assert so.idlm_isd_loop_step(ctypes.byref(d), *args(None, None, fake)) == 1
+    assert so.idlm_isd_loop_step(ctypes.byref(d), *args(None, fake, None)) == 1
+    z = good(B=0)
+    assert so.idlm_isd_loop_step(ctypes.byref(z), None, None, None, None, None, None, None, None,
+                                 None, 1, 4, f, None, None, None, None, None, fake,
+                                 L.idlm_isd_workspace_bytes(z), None) == 0
+
+
 def test_mask_stats_bytes(so):
     # header (256) + each MASK row's (max, sum) [B][K] + logits and drafts [B][K]
     d = good()

@@ -212,3 +212,50 @@ def test_loop_with_mask_stats_matches_plain_acceptance(torch_cuda, T):
     flagged = L.idlm_isd_read_status(ws)
     verifying = bool((nxt[:, 0] >= 0).any().item())
     assert flagged == (7 if verifying else 0)
+
+
+def test_loop_step_equals_step_then_propose(torch_cuda):
+    """idlm_isd_loop_step (proposals on the acceptance's stream, beside the
+    attention) against idlm_isd_step then idlm_isd_propose: attention
+    output, tokens, lengths, next drafts and the MASK-row statistics record
+    bit-identical, over two iterations, the second reading and rewriting one
+    record in place."""
+    torch = torch_cuda
+    from speculative_verify_isd_amd import lib as L
+    from speculative_verify_isd_amd.lib import DeviceStep
+
+    w = W.named_workload("b16", 1)  # B*R*V = 17M logits: the step forks
+    rng = np.random.default_rng(9)
+    nxt_rows = [_dev(torch, W.f32_to_bf16_bits(rng.normal(0, 3, w.logits_mask.shape)
+                                               .astype(np.float32)), "bf16") for _ in range(2)]
+    B, K = w.B, w.N - 1
+    a, b = DeviceStep(w), DeviceStep(w)
+    ms_a = [L.alloc_mask_stats(a.dims), L.alloc_mask_stats(a.dims)]
+    ms_b = L.alloc_mask_stats(b.dims)
+    drafts_a, drafts_b = a.drafts.clone(), b.drafts.clone()
+    nxt_a = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    nxt_b = torch.empty_like(nxt_a)
+    for it in range(2):
+        seed = 40 + it
+        rec_in_a = ms_a[1 - it % 2] if it else None
+        rec_in_b = ms_b if it else None
+        a.step(seed=seed, drafts=drafts_a, mask_stats=rec_in_a)
+        L.idlm_isd_propose(a.dims, nxt_rows[it], drafts_a, a.lens, seed, w.T, nxt_a, a.ws,
+                           mask_stats=ms_a[it % 2])
+        L.idlm_isd_loop_step(b.dims, b.q, b.kv, b.page_table, b.ctx_lens, b.lc, b.lm, drafts_b,
+                             rec_in_b, nxt_rows[it], seed, w.N, w.T, b.tokens, b.lens, b.out,
+                             nxt_b, ms_b, b.ws)
+        torch.cuda.synchronize()
+        assert L.idlm_isd_read_status(a.ws) == 0 and L.idlm_isd_read_status(b.ws) == 0
+        for name, x, y in (("out", a.out, b.out), ("tokens", a.tokens, b.tokens),
+                           ("lens", a.lens, b.lens), ("next", nxt_a, nxt_b),
+                           ("record", ms_a[it % 2], ms_b)):
+            bx = x.contiguous().view(torch.uint8).cpu().numpy().tobytes()
+            by = y.contiguous().view(torch.uint8).cpu().numpy().tobytes()
+            assert bx == by, (it, name)
+        # next iteration: these drafts verified against the rows they came from
+        a.lm, b.lm = nxt_rows[it], nxt_rows[it]
+        drafts_a.copy_(nxt_a)
+        drafts_b.copy_(nxt_b)
+    print(f"[loop] loop step = step + propose over 2 iterations, "
+          f"{int((nxt_b[:, 0] >= 0).sum().item())} sequences verifying next", flush=True)
