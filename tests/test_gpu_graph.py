@@ -64,3 +64,64 @@ def test_step_graph_replays_match_eager(torch_cuda, T, V):
         assert torch.equal(ds.out.view(torch.int16), ref[2].view(torch.int16)), f"replay {i}: attention"
         assert torch.isfinite(noise)
     print(f"[graph] T={T} V={V}: 4 replays identical to the eager step", flush=True)
+
+
+def test_loop_step_graph_replays_match_eager(torch_cuda):
+    """idlm_isd_loop_step captured with a MASK-row statistics record as input
+    and another as output (proposals forked beside the attention): every
+    replay reproduces the eager call's tokens, lengths, attention output,
+    next drafts and output record bit for bit."""
+    torch = torch_cuda
+    from speculative_verify_isd_amd import lib as L
+    from speculative_verify_isd_amd.lib import DeviceStep
+
+    rng = np.random.default_rng(43)
+    ctx = rng.integers(600, 3000, size=8, endpoint=True)
+    w = W.make_workload("graph_loop", B=8, N=4, Hq=32, Hkv=8, D=128, V=151936, ctx_lens=ctx,
+                        T=1.0, seed=6)
+    ds = DeviceStep(w)
+    K = w.N - 1
+    rec_in, rec_out = L.alloc_mask_stats(ds.dims), L.alloc_mask_stats(ds.dims)
+    drafts = torch.empty((w.B, K), dtype=torch.int32, device="cuda")
+    nxt = torch.empty_like(drafts)
+    fresh = torch.full_like(drafts, -1)
+    ones = torch.ones(w.B, dtype=torch.int32, device="cuda")
+    # the drafts to verify, and their record, from the MASK rows
+    L.idlm_isd_propose(ds.dims, ds.lm, fresh, ones, 3, w.T, drafts, ds.ws, mask_stats=rec_in)
+    nxt_rows = torch.flip(ds.lm, dims=[0]).contiguous()
+
+    def call():
+        L.idlm_isd_loop_step(ds.dims, ds.q, ds.kv, ds.page_table, ds.ctx_lens, ds.lc, ds.lm,
+                             drafts, rec_in, nxt_rows, 77, w.N, w.T, ds.tokens, ds.lens, ds.out,
+                             nxt, rec_out, ds.ws)
+
+    call()
+    torch.cuda.synchronize()
+    assert L.idlm_isd_read_status(ds.ws) == 0
+    outs = lambda: [t.contiguous().view(torch.uint8).clone() for t in
+                    (ds.tokens, ds.lens, ds.out, nxt, rec_out)]
+    ref = outs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in range(4):
+        for t in (ds.tokens, ds.lens, nxt):
+            t.fill_(-7)
+        ds.out.zero_()
+        rec_out.fill_(0)
+        noise = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(("tokens", "lens", "out", "next", "record"), outs(), ref):
+            assert torch.equal(x, y), f"replay {i}: {name}"
+        assert torch.isfinite(noise)
+    assert L.idlm_isd_read_status(ds.ws) == 0
+    print("[graph] loop step: 4 replays identical to the eager call", flush=True)
