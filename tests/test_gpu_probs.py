@@ -9,8 +9,9 @@
   Language Models", section "Inference & ISD").
 * Thousands of residual and bonus draws over 151936-entry rows at
   sigma = 0.1, where p and q nearly cancel and the residual is the hardest
-  to sample exactly: no committed token may differ from the oracle's unless
-  its threshold lies within the boundary band.
+  to sample exactly, and residual draws at sigma = 0.5, T = 0.7 (the N = 8
+  workload's temperature): no committed token may differ from the oracle's
+  unless its threshold lies within the boundary band.
 """
 
 from concurrent.futures import ThreadPoolExecutor
@@ -114,16 +115,17 @@ def _pinned_drafts(w, keep):
     return out
 
 
-@pytest.mark.parametrize("mode", ["residual", "bonus"])
-def test_many_draws_sigma_0_1_full_vocabulary(torch_cuda, mode):
+@pytest.mark.parametrize("mode,sigma,T", [("residual", 0.1, 1.0), ("bonus", 0.1, 1.0),
+                                          ("residual", 0.5, 0.7)])
+def test_many_draws_full_vocabulary(torch_cuda, mode, sigma, T):
     from speculative_verify_isd_amd.lib import DeviceStep
 
     B, N, seeds = 64, 8, 64
     w = W.make_workload(f"draws_{mode}", B=B, N=N, Hq=8, Hkv=8, D=64, V=W.VOCAB,
-                        ctx_lens=[2 * N] * B, T=1.0, seed=91 if mode == "residual" else 92,
-                        sigma=0.1)
+                        ctx_lens=[2 * N] * B, T=T,
+                        seed=(91 if mode == "residual" else 92) + int(10 * sigma), sigma=sigma)
     w = dataclasses.replace(w, draft_tokens=_pinned_drafts(w, keep=(mode == "bonus")))
-    print(f"[case] {w.name} B={B} N={N} V={w.V} sigma=0.1 seeds={seeds}", flush=True)
+    print(f"[case] {w.name} B={B} N={N} V={w.V} sigma={sigma} T={T} seeds={seeds}", flush=True)
     rows = _rows(w, t32(w.T))
     ds = DeviceStep(w)
     K = N - 1
