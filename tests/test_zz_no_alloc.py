@@ -77,3 +77,40 @@ def test_noalloc_flags_bad_drafts(torch_cuda):
                          seed=7)
     _, ref_status, _, status = _both(torch, w2, 22, 1.0)
     assert ref_status == 0 and status == 0
+
+
+def test_noalloc_at_its_largest_batch(torch_cuda):
+    """The largest batch the static scratch holds at N = 4, V = 151936
+    (B = 1469; one more is refused with IDLM_ERR_SCRATCH, checked on the
+    host): bit-identical to idlm_isd_accept.  Logits are seeded N(0, 3^2) bf16 made on the device,
+    clean rows perturbed by N(0, 0.5^2); drafts drawn uniformly."""
+    torch = torch_cuda
+    from speculative_verify_isd_amd import lib as L
+
+    B, N, V = 1469, 4, W.VOCAB
+    K = N - 1
+    dims = L.make_dims(B, N, 8, 8, 64, V, 1, 1, "bf16", "bf16")
+    print(f"[case] noalloc largest batch B={B} N={N} V={V}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(1469)
+    lm = (torch.randn((B, K, V), generator=g, device="cuda") * 3).to(torch.bfloat16)
+    lc = torch.empty((B, N, V), dtype=torch.bfloat16, device="cuda")
+    lc[:, :K] = (lm.float() + 0.5 * torch.randn((B, K, V), generator=g, device="cuda")).to(
+        torch.bfloat16)
+    lc[:, K] = (torch.randn((B, V), generator=g, device="cuda") * 3).to(torch.bfloat16)
+    drafts = torch.randint(0, V, (B, K), generator=g, device="cuda", dtype=torch.int32)
+    ws = L.alloc_workspace(dims)
+    tok_a = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    len_a = torch.empty(B, dtype=torch.int32, device="cuda")
+    dbg_a = torch.empty((B, N + 1, 4), dtype=torch.float64, device="cuda")
+    tok_b, len_b, dbg_b = torch.full_like(tok_a, -9), torch.full_like(len_a, -9), \
+        torch.full_like(dbg_a, 7.0)
+    status = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    L.idlm_isd_accept(dims, lc, lm, drafts, 5, 1.0, tok_a, len_a, dbg_a, ws)
+    L.idlm_isd_accept_noalloc(dims, lc, lm, drafts, 5, 1.0, tok_b, len_b, dbg_b, status)
+    torch.cuda.synchronize()
+    assert L.idlm_isd_read_status(ws) == 0 and int(status.item()) == 0
+    for name, x, y in (("tokens", tok_a, tok_b), ("lens", len_a, len_b), ("debug", dbg_a, dbg_b)):
+        assert x.cpu().numpy().tobytes() == y.cpu().numpy().tobytes(), name
+    mean_len = float(len_a.float().mean().item())
+    print(f"[noalloc] B={B}: identical to the workspace call; mean accept length {mean_len:.3f}",
+          flush=True)
