@@ -34,7 +34,8 @@
 //                      and both over the elements where p > q by the row
 //                      statistics.  With every draft kept it sums the bonus
 //                      row's 2^((l - m) c) per sub-chunk instead.  These
-//                      exponentials are float64 (exp2d).
+//                      exponentials are float64 (exp2t, from a table of
+//                      2^(j/64) in LDS).
 //   accept_select      grid B.  The exact ratio S_p/S_q turns the residual
 //                      sums into sub-chunk weights (bonus: the bonus row's
 //                      sub-chunk sums); wave 0 prefixes them and finds the
@@ -42,6 +43,13 @@
 //                      it in float64 (8 consecutive elements each) and a block
 //                      prefix finds the smallest v whose running sum exceeds
 //                      t.
+//
+// With the MASK-row statistics the proposals recorded for these drafts
+// (the decode loop: MASK rows propose with q, and the same q tests the
+// drafts one step later), accept_stats reduces only the N clean rows and the
+// decision reads each MASK row's (max, sum) and the drafts' logits from the
+// record, after checking it was made for these drafts, this T and these
+// sizes.
 //
 // Float64 sampling weights: the token is the smallest v whose running sum of
 // w passes t.  Float32 exponentials move those running sums by ~1e-7 of the
