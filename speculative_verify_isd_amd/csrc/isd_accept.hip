@@ -114,7 +114,9 @@ struct AccArgs {
   uint64_t seed;
   float c2;      // log2(e) / T as float32 (row statistics)
   double c2d;    // log2(e) / T as float64 (sampling weights)
+  double c64;    // 64 c2d (exact): exp2t64's argument scale
   Exp2Coef cf;   // exp2d's coefficients (kept in scalar registers)
+  Exp2Coef64 cf64;
   int greedy;    // T == 0
   int32_t* out_tokens;
   int32_t* out_len;
@@ -211,10 +213,12 @@ __device__ inline double wave_total(double x) {
   return x;
 }
 
-// 2^((l - m) c) in float64, c = log2(e) / T, with exp2t and the
-// work-group's table of 2^(j/64) in LDS.
+// 2^((l - m) c) in float64, c = log2(e) / T, with the work-group's table of
+// 2^(j/64) in LDS: exp2t64 of 64 (l - m) c, bit-identical to exp2t of
+// (l - m) c.  m is the row's maximum (from the statistics or the proposals'
+// record), so the argument is never positive, as exp2t64 requires.
 __device__ inline double wexp(const AccArgs& a, const double* tab, float l, double m) {
-  return exp2t(((double)l - m) * a.c2d, tab, a.cf);
+  return exp2t64(((double)l - m) * a.c64, tab, a.cf64);
 }
 
 // v[i] for a run-time i in [0, 4), by selects (no indexed register array).
@@ -598,12 +602,13 @@ __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
       for (int e = 0; e < 8; ++e) {
         const double ep = wexp(a, sh_tab, xp[k][e], sp.mp);
         const double eq = wexp(a, sh_tab, xq[k][e], sp.mq);
+        // 1 or 0: e times it added by an fma is e added or nothing, in one
+        // instruction per sum instead of a 64-bit select and an add
+        const double in = ep > sp.rho * eq ? 1.0 : 0.0;
         v[0] += ep;
         v[1] += eq;
-        if (ep > sp.rho * eq) {
-          v[2] += ep;
-          v[3] += eq;
-        }
+        v[2] = fma(ep, in, v[2]);
+        v[3] = fma(eq, in, v[3]);
       }
     } else {
       // Bonus row (clean row k): e = 2^((l - m) c) relative to the row max.
@@ -941,7 +946,9 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
   a.greedy = (T == 0.0f);
   a.c2 = a.greedy ? 0.f : (float)(1.4426950408889634 / (double)T);
   a.c2d = a.greedy ? 0.0 : 1.4426950408889634 / (double)T;
+  a.c64 = 64.0 * a.c2d;
   a.cf = kExp2Coef;
+  a.cf64 = kExp2Coef64;
   a.out_tokens = out_tokens;
   a.out_len = out_len;
   a.debug = out_debug;

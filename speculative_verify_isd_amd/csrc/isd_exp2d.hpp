@@ -93,4 +93,36 @@ IDLM_HD inline double exp2t(double y, const double* tab, const Exp2Coef& k) {
   return ldexp(p * tab[ki & 63], ki >> 6);
 }
 
+// exp2t64: exp2t with the argument given as z = 64 y, for callers that fold
+// the factor 64 into their own scale and whose y is never positive (a weight
+// relative to its row maximum).  With s = z - k = 64 r the polynomial runs
+// in s on the coefficients (ln 2)^j / j! / 64^j; every step of it is the
+// corresponding step of exp2t scaled by a power of two, so the result is
+// bit-identical to exp2t(z / 64) for z <= 0, in two fewer instructions (the
+// scaling and the upper clamp).  z is clamped below at -70400 (y = -1100;
+// a NaN z gives 0).
+struct Exp2Coef64 {
+  double c[6];
+};
+
+constexpr Exp2Coef64 kExp2Coef64 = {{1.0, exp2d_detail::coef(1) / 64.0,
+                                     exp2d_detail::coef(2) / 4096.0,
+                                     exp2d_detail::coef(3) / 262144.0,
+                                     exp2d_detail::coef(4) / 16777216.0,
+                                     exp2d_detail::coef(5) / 1073741824.0}};
+
+IDLM_HD inline double exp2t64(double z, const double* tab, const Exp2Coef64& k) {
+  z = fmax(z, -70400.0);
+  const double kk = rint(z);
+  const double s = z - kk;  // exact, |s| <= 1/2
+  const int ki = (int)kk;
+  double p = k.c[5];
+  p = fma(p, s, k.c[4]);
+  p = fma(p, s, k.c[3]);
+  p = fma(p, s, k.c[2]);
+  p = fma(p, s, k.c[1]);
+  p = fma(p, s, 1.0);
+  return ldexp(p * tab[ki & 63], ki >> 6);
+}
+
 }  // namespace idlm

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <string.h>
 
 #include "isd_exp2d.hpp"
 
@@ -45,6 +46,44 @@ int main() {
   printf("t_at_m1 %.17g\n", idlm::exp2t(-1.0, tab, idlm::kExp2Coef));
   printf("t_at_m1075 %.17g\n", idlm::exp2t(-1075.5, tab, idlm::kExp2Coef));
   printf("t_at_nan %.17g\n", idlm::exp2t(NAN, tab, idlm::kExp2Coef));
+  // exp2t64 (argument 64 y, scaled coefficients): bit-identical to exp2t for
+  // y <= 0.  Sweep: the sampler's form y = d * c with d a difference of two
+  // bf16-like values and c a random log2(e)/T, plus the whole range down to
+  // past the underflow, and the special values.
+  s = 777;
+  long mism = 0, count = 0;
+  auto same = [&](double y) {
+    const double a = idlm::exp2t(y, tab, idlm::kExp2Coef);
+    const double b = idlm::exp2t64(y * 64.0, tab, idlm::kExp2Coef64);
+    uint64_t ua, ub;
+    memcpy(&ua, &a, 8);
+    memcpy(&ub, &b, 8);
+    mism += ua != ub;
+    ++count;
+  };
+  for (int i = 0; i < 2000000; ++i) {
+    const double r = (double)(splitmix(s) >> 11) * 0x1.0p-53;
+    const double r2 = (double)(splitmix(s) >> 11) * 0x1.0p-53;
+    const double r3 = (double)(splitmix(s) >> 11) * 0x1.0p-53;
+    auto bf16 = [](double x) {
+      const float f = (float)x;
+      uint32_t bits;
+      memcpy(&bits, &f, 4);
+      bits &= 0xFFFF0000u;
+      float g;
+      memcpy(&g, &bits, 4);
+      return (double)g;
+    };
+    const double m = bf16(20.0 * r3 - 10.0);         // the row maximum
+    const double l = bf16(m - 30.0 * r);              // an element at or below it
+    const double c = 1.4426950408889634 / (0.05 + 4.0 * r2);
+    if (l <= m) same((l - m) * c);
+    same(-1120.0 * r);
+  }
+  const double specials[] = {0.0, -0.0, -1e-300, -0x1.0p-1074, -1.0 / 128, -1.0 / 64, -0.5,
+                             -1022.0, -1074.0, -1075.5, -1100.0, -1e6, -INFINITY, NAN};
+  for (double y : specials) same(y);
+  printf("t64_mismatch %ld\nt64_count %ld\n", mism, count);
   printf("at_0 %.17g\n", idlm::exp2d(0.0));
   printf("at_1 %.17g\n", idlm::exp2d(1.0));
   printf("at_m1 %.17g\n", idlm::exp2d(-1.0));

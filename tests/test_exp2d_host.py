@@ -48,3 +48,10 @@ def test_table_variant(results):
     assert results["worst_rel_t"] < 4.5e-16, results
     assert results["t_at_0"] == 1.0 and results["t_at_m1"] == 0.5
     assert results["t_at_m1075"] == 0.0 and results["t_at_nan"] == 0.0
+
+
+def test_scaled_table_variant_is_bit_identical(results):
+    # exp2t64 takes 64 y and power-of-two-scaled coefficients: every step is
+    # exp2t's step times a power of two, so the bits agree for y <= 0
+    assert results["t64_count"] > 4e6
+    assert results["t64_mismatch"] == 0, results
