@@ -31,6 +31,10 @@ b16    as b1 with B=16, ctx ~ U[1024, 8192], one shared pool with 10% slack
 c64    as b1 with B=64, ctx ~ U[2048, 16384], sigma in {0.1, 0.5, 1.5}.
 c64n8  B=64, N=8, 64/8 heads, D=128, bfloat16, ctx ~ U[4096, 32768],
        sigma = 0.5, T=0.7.
+
+One GPU's share of c64 on eight GPUs:
+c64_dp8  split by sequence: B=8 with the first 8 of c64's contexts.
+c64_tp8  split by KV head: B=64 with c64's contexts, 4/1 heads.
 """
 
 import os
@@ -240,9 +244,11 @@ CALIBRATED_SIGMAS = (0.074, 0.25, 1.07)
 
 
 def named_workload(name, sigma_index=1, sigma=None):
-    """The five named workloads of the module docstring.  For c64, ``sigma``
-    replaces the swept value SIGMAS[sigma_index] (same contexts and seeds;
-    CALIBRATED_SIGMAS give the acceptance rates the configuration names)."""
+    """The five named workloads of the module docstring, plus one GPU's share
+    of the C = 64 step on eight GPUs (c64_dp8 by sequence, c64_tp8 by KV
+    head).  For the C = 64 workloads, ``sigma`` replaces the swept value
+    SIGMAS[sigma_index] (same contexts and seeds; CALIBRATED_SIGMAS give the
+    acceptance rates the configuration names)."""
     if name == "tiny":
         return make_workload("tiny", B=1, N=4, Hq=8, Hkv=2, D=64, V=512, ctx_lens=[256],
                              T=1.0, seed=1000, qkv_dtype="f32", logits_dtype="f32",
@@ -262,6 +268,21 @@ def named_workload(name, sigma_index=1, sigma=None):
         sigma = SIGMAS[sigma_index] if sigma is None else float(sigma)
         return make_workload(f"{label}{sigma}", B=64, N=4, Hq=32, Hkv=8, D=128, V=VOCAB,
                              ctx_lens=ctx, T=1.0, seed=4000 + sigma_index, sigma=sigma,
+                             max_pages=16384 // PAGE)
+    if name in ("c64_dp8", "c64_tp8"):
+        # One GPU's share of the C = 64 step on eight GPUs.  dp8: split by
+        # sequence, the first 8 of the same context draws (the step needs no
+        # exchange across GPUs).  tp8: split by KV head, all 64 sequences with
+        # one KV head and its 4 query heads (the attention's share; the
+        # vocabulary-split acceptance would need a cross-GPU exchange).
+        ctx = rng.integers(2048, 16384, size=64, endpoint=True)
+        sigma = SIGMAS[sigma_index] if sigma is None else float(sigma)
+        if name == "c64_dp8":
+            return make_workload(f"c64_dp8_s{sigma}", B=8, N=4, Hq=32, Hkv=8, D=128, V=VOCAB,
+                                 ctx_lens=ctx[:8], T=1.0, seed=4100 + sigma_index, sigma=sigma,
+                                 max_pages=16384 // PAGE)
+        return make_workload(f"c64_tp8_s{sigma}", B=64, N=4, Hq=4, Hkv=1, D=128, V=VOCAB,
+                             ctx_lens=ctx, T=1.0, seed=4200 + sigma_index, sigma=sigma,
                              max_pages=16384 // PAGE)
     if name == "c64n8":
         ctx = rng.integers(4096, 32768, size=64, endpoint=True)

@@ -328,7 +328,8 @@ def _picks(w, n, seed):
             for k, b in enumerate(bs)]
 
 
-@pytest.mark.parametrize("name,sig", [("b1", 1), ("b16", 1), ("c64", 1), ("c64n8", 1)])
+@pytest.mark.parametrize("name,sig", [("b1", 1), ("b16", 1), ("c64", 1), ("c64n8", 1),
+                                      ("c64_dp8", 1), ("c64_tp8", 1)])
 def test_named_full_size_every_head_vector(torch_cuda, name, sig):
     """Every attention head vector of the named workload against the oracle
     (every (b, KV head) pair and every merge of its split pieces), and every
