@@ -551,10 +551,10 @@ __device__ inline void block_total4(double v[4], double (*red)[4]) {
 // ---------------------------------------------------------------------------
 // Kernel 2: decision + the residual pair's float64 sums per sub-chunk.
 // ---------------------------------------------------------------------------
-#ifndef ACCEPT_SPW
-#define ACCEPT_SPW 4
-#endif
-constexpr int kMaxSpw = ACCEPT_SPW;  // most sub-chunks one summing work-group takes
+constexpr int kMaxSpw = 2;  // most sub-chunks one summing work-group takes
+// Batches of at most this many sub-chunks (about eight work-groups per CU)
+// take one sub-chunk per summing work-group.
+constexpr int64_t kOneSubMax = 2048;
 
 template <bool VEC, bool F32>
 __global__ __launch_bounds__(256) void accept_decide_sum_kernel(AccArgs a) {
@@ -861,16 +861,23 @@ int32_t launch_stats(const AccArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? IDLM_OK : IDLM_ERR_HIP;
 }
 
-// Sub-chunks per summing work-group: kMaxSpw (every work-group repeats the
-// decision, and fewer, larger work-groups measured faster at C = 64 while the
-// grid still fits on the chip at once up to about a hundred sequences).
-inline int sums_per_wg(int nsub, bool greedy) { return greedy ? nsub : std::min(kMaxSpw, nsub); }
+// Sub-chunks per summing work-group.  The float64 sums are bound by the
+// vector ALUs, so small batches spread them over as many work-groups as
+// there are sub-chunks (b1 25.5 -> 19.2 us per acceptance against four per
+// work-group, b16 38.6 -> 35.1, B = 8 of C = 64 32.4 -> 28.3); C = 64 is
+// fastest at two (56.5 us, against 57.8 at one or four), where every
+// work-group repeating the decision starts to weigh.  Greedy: the decision
+// alone, one work-group per sequence.
+inline int sums_per_wg(int64_t B, int nsub, bool greedy) {
+  if (greedy) return nsub;
+  return std::min(B * nsub <= kOneSubMax ? 1 : kMaxSpw, nsub);
+}
 
 template <bool VEC, bool F32>
 int32_t launch_all(AccArgs a, hipStream_t s) {
   const int32_t r = launch_stats<kStatsU, VEC, F32>(a, s);
   if (r != IDLM_OK) return r;
-  a.spw = sums_per_wg(a.nsub, a.greedy);
+  a.spw = sums_per_wg(a.B, a.nsub, a.greedy);
   a.S2 = (a.nsub + a.spw - 1) / a.spw;
   const int64_t g2 = (int64_t)a.B * a.S2;
   hipLaunchKernelGGL((accept_decide_sum_kernel<VEC, F32>), dim3((unsigned)g2), dim3(256), 0, s, a);
@@ -928,7 +935,8 @@ int64_t accept_max_grid(const idlm_isd_dims& d) {
   const int64_t S1 = (d.V + (int64_t)kSub * kStatsU - 1) / ((int64_t)kSub * kStatsU);
   const int nsub = (int)((d.V + kSub - 1) / kSub);
   const int64_t stats = (int64_t)d.B * R * S1;
-  const int64_t sums = (int64_t)d.B * ((nsub + sums_per_wg(nsub, false) - 1) / sums_per_wg(nsub, false));
+  const int spw = sums_per_wg(d.B, nsub, false);
+  const int64_t sums = (int64_t)d.B * ((nsub + spw - 1) / spw);
   return std::max(stats, sums);
 }
 
