@@ -188,10 +188,11 @@ size_t idlm_isd_mask_stats_bytes(const idlm_isd_dims* d);
  *                  it made draft_tokens from logits_mask at this T.  The MASK
  *                  rows' maxima and sums and the drafts' logits then come
  *                  from it, and logits_mask is read only for a rejected
- *                  draft's residual.  q differs from a reduction of
- *                  logits_mask by float64 rounding only (the proposals
- *                  merge their 2048-logit sub-chunks, the acceptance its
- *                  8192-logit slices).
+ *                  draft's residual.  The record's sums are float64
+ *                  weights at the float64 scale log2(e)/T; the
+ *                  acceptance's own reduction sums float32 exponentials
+ *                  at that scale rounded to float32, so q from either
+ *                  agrees to about 1e-7 relative.
  * Draft i is kept iff p_i(x) > 0 and (p_i(x) >= q_i(x) or u_i*q_i(x) <
  * p_i(x)), in float64.  At the first rejected index j the token is the
  * smallest v whose running sum of w = max(0, p_j - q_j) exceeds
@@ -302,7 +303,8 @@ int32_t idlm_isd_loop_step(const idlm_isd_dims* d, const void* q, const void* kv
  * i of its next step is drawn from softmax(logits_next[b][i] / T) by inverse
  * CDF (ascending vocabulary, smallest v whose running sum exceeds u * sum)
  * with u = word 0 of the Philox4x64-10 block at counter (i, 1, 0, 0) under
- * key (seed, b), or the argmax (lowest index) when T == 0.  Otherwise the
+ * key (seed, b), or the argmax (lowest index) when T == 0; the weights are
+ * float64 (exponentials included), as are the running sums.  Otherwise the
  * next step is fresh and all its drafts are -1.  No-op when N == 1.
  *   logits_next  [device] [B][K][V] logits_dtype: this forward's MASK rows
  *   draft_tokens [device] int32 [B][K]: this step's list

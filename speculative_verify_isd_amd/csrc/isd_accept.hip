@@ -1036,10 +1036,11 @@ namespace {
 // uniform of Philox counter (i, 1, 0, 0); T = 0 takes the argmax.  Otherwise
 // the next step is fresh and its drafts are all -1.
 //
-//   propose_stats   grid B*K*ceil(nsub/8): each wave reduces whole 2048-element
-//                   sub-chunks to (max m_c, sum of exp2((l - m_c) c)) (greedy:
-//                   max, lowest argmax).  Rows of sequences that will not
-//                   continue are skipped, so their logits are never read.
+//   propose_stats   grid B*K*ceil(nsub/4): each wave reduces one 2048-element
+//                   sub-chunk to (max m_c, float64 sum of 2^((l - m_c) c),
+//                   each weight a table exponential exp2t64) (greedy: max,
+//                   lowest argmax).  Rows of sequences that will not continue
+//                   are skipped, so their logits are never read.
 //   propose_select  grid B*K, four waves per row: wave 0 takes the weights
 //                   s_c * 2^((m_c - M) c) in sub-chunk order and a wave scan
 //                   locates the sub-chunk holding t = u * total; all 256
@@ -1057,7 +1058,11 @@ struct PropArgs {
   float* mdlog;             // [B][K]
   int32_t* mtok;            // [B][K]
   uint64_t seed;
-  float c2;                 // log2(e) / T
+  float c2;                 // log2(e) / T as float32 (identifies T in the record)
+  double c2d;               // log2(e) / T as float64 (sampling weights)
+  double c64;               // 64 c2d (exact): exp2t64's argument scale
+  Exp2Coef cf;              // for the table of 2^(j/64)
+  Exp2Coef64 cf64;
   int greedy, B, K, V, nsub, f32;
 };
 
@@ -1082,7 +1087,11 @@ __device__ inline void put_draft(const PropArgs& a, int b, int i, int tok) {
   }
 }
 
-constexpr int kPropSubPerWave = 2;
+// Sub-chunks per wave of propose_stats.  Its float64 weights are bound by
+// the vector ALUs and only continuing sequences' rows have work, so one
+// sub-chunk per wave spreads them best (c64: 25.8 us per call against 32.6
+// with two; float32 weights took 19.9).
+constexpr int kPropSubPerWave = 1;
 
 // Whether sequence b's next step verifies (all listed drafts kept).
 __device__ inline bool continues(const PropArgs& a, int b) {
@@ -1121,6 +1130,11 @@ __global__ __launch_bounds__(256) void propose_stats_kernel(PropArgs a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) x[k][g] = load8<VEC, F32>(row, sc * kSub + 512 * g + 8 * lane, a.V);
   }
+  __shared__ double sh_tab[64];  // 2^(j/64), built while the loads are in flight
+  if (!a.greedy) {
+    if (threadIdx.x < 64) sh_tab[threadIdx.x] = exp2t_entry((int)threadIdx.x, a.cf);
+    __syncthreads();
+  }
 #pragma unroll
   for (int k = 0; k < kPropSubPerWave; ++k) {
     const int sc = sc0 + k;
@@ -1150,15 +1164,15 @@ __global__ __launch_bounds__(256) void propose_stats_kernel(PropArgs a) {
         for (int e = 0; e < 8; ++e) m = fmaxf(m, x[k][g][e]);
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      // float64 weights 2^((l - m_c) c) relative to the sub-chunk max (the
+      // rescan in propose_select evaluates the same expression).
       double s = 0.0;
       if (m != -INFINITY) {
+        const double md = (double)m;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float part = 0.f;
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) part += __builtin_amdgcn_exp2f((x[k][g][e] - m) * a.c2);
-          s += (double)part;
-        }
+          for (int e = 0; e < 8; ++e) s += exp2t64(((double)x[k][g][e] - md) * a.c64, sh_tab, a.cf64);
       }
       s = wave_total(s);
       if (lane == 0) out[sc] = make_double2((double)m, s);
@@ -1173,6 +1187,7 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
   __shared__ float sh_mc;
   __shared__ double sh_wsum[4];
   __shared__ int sh_last[4];
+  __shared__ double sh_tab[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x / a.K, i = blockIdx.x % a.K;
   if (!continues(a, b)) {
@@ -1206,7 +1221,7 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
     // Wave 0 locates the sub-chunk: weights s_c 2^((m_c - M) c) in order,
     // each lane a contiguous run, a wave scan, the first sub-chunk with
     // positive weight whose end exceeds t = u * W.
-    const double c2 = (double)a.c2;
+    const double c2 = a.c2d;
     double M = -INFINITY;
     for (int k = k0; k < k1; ++k) M = fmax(M, st[k].x);
 #pragma unroll
@@ -1265,6 +1280,7 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
       if (a.mrow) a.mrow[(size_t)b * a.K + i] = make_double2(M, W);  // the row's (max, sum)
     }
   }
+  if (tid < 64) sh_tab[tid] = exp2t_entry(tid, a.cf);
   __syncthreads();
   const int sc = sh_sc, past = sh_past;
   const double tl = sh_tl;
@@ -1274,17 +1290,16 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
   const void* row = prop_row(a, b, i);
   const int v0 = sc * kSub + 8 * tid;
   const Logits8<VEC, F32> xs = load8<VEC, F32>(row, v0, a.V);
-  float w[8];
-  float part = 0.f;
+  double w[8];
+  double part = 0.0;
   int lastp = -1;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float x = xs[e];
-    w[e] = x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((x - mc) * a.c2);
+    w[e] = exp2t64(((double)xs[e] - (double)mc) * a.c64, sh_tab, a.cf64);
     part += w[e];
-    if (w[e] > 0.f) lastp = v0 + e;
+    if (w[e] > 0.0) lastp = v0 + e;
   }
-  double inc = (double)part;
+  double inc = part;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const double y = __shfl_up(inc, off);
@@ -1308,7 +1323,7 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
     bool done = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      r += (double)w[e];
+      r += w[e];
       if (!done && r > tl) {
         tok = v0 + e;
         done = true;
@@ -1363,6 +1378,10 @@ int32_t launch_propose(const idlm_isd_dims& d, const Plan& p, const void* logits
   a.seed = seed;
   a.greedy = (T == 0.0f);
   a.c2 = a.greedy ? 0.f : (float)(1.4426950408889634 / (double)T);
+  a.c2d = a.greedy ? 0.0 : 1.4426950408889634 / (double)T;
+  a.c64 = 64.0 * a.c2d;
+  a.cf = kExp2Coef;
+  a.cf64 = kExp2Coef64;
   a.B = d.B;
   a.K = d.N - 1;
   a.V = d.V;
