@@ -1339,10 +1339,11 @@ __global__ __launch_bounds__(256) void propose_select_kernel(PropArgs a) {
   }
 }
 
+constexpr int kPropSubPerWg = 4 * kPropSubPerWave;
+
 template <bool VEC, bool F32>
 int32_t launch_propose_t(PropArgs a, hipStream_t s) {
-  constexpr int kSubPerWg = 4 * kPropSubPerWave;
-  const int S = (a.nsub + kSubPerWg - 1) / kSubPerWg;
+  const int S = (a.nsub + kPropSubPerWg - 1) / kPropSubPerWg;
   const int64_t g1 = (int64_t)a.B * a.K * S;
   hipLaunchKernelGGL((propose_stats_kernel<VEC, F32>), dim3((unsigned)g1), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return IDLM_ERR_HIP;
@@ -1356,6 +1357,12 @@ int32_t launch_propose_t(PropArgs a, hipStream_t s) {
 }  // namespace idlm
 
 namespace idlm {
+
+int64_t propose_max_grid(const idlm_isd_dims& d) {
+  const int64_t nsub = (d.V + kSub - 1) / kSub;
+  const int64_t stats = (int64_t)d.B * (d.N - 1) * ((nsub + kPropSubPerWg - 1) / kPropSubPerWg);
+  return std::max(stats, (int64_t)d.B * (d.N - 1));
+}
 
 int32_t launch_propose(const idlm_isd_dims& d, const Plan& p, const void* logits_next,
                        const int32_t* drafts, const int32_t* accept_len, uint64_t seed, float T,

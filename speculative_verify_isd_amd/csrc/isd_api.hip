@@ -91,12 +91,11 @@ int32_t check_dims(const idlm_isd_dims* d) {
   // and float32 kernels (one work-group per (b, KV head)), the acceptance
   // (greedy and sampled), its probability dump, the proposals and the KV
   // scatter (one work-item per 8 dims of a row's head).
-  const int64_t B = d->B, K = d->N - 1;
-  const int64_t nsub = ceil_div(d->V, kSub);
+  const int64_t B = d->B;
   bool ok = grid_fits(B * d->Hkv, 256);
   ok = ok && grid_fits(accept_max_grid(*d), 256);
   ok = ok && grid_fits(B * R * ceil_div(d->V, 4096), 256);
-  ok = ok && grid_fits(B * K * ceil_div(nsub, 8), 256);
+  ok = ok && grid_fits(propose_max_grid(*d), 256);
   ok = ok && grid_fits(B * R * d->Hkv * (d->D / 8), 1);
   if (!ok) return IDLM_ERR_UNSUPPORTED;
   return IDLM_OK;

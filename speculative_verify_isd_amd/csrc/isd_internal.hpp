@@ -113,6 +113,7 @@ int32_t launch_accept(const idlm_isd_dims& d, const Plan& p, const void* lc, con
 // Work-groups of the acceptance's launches (stats, decide + sums, select),
 // the largest of the three.  Host only; shared by validation and launch.
 int64_t accept_max_grid(const idlm_isd_dims& d);
+int64_t propose_max_grid(const idlm_isd_dims& d);  // work-groups of the largest proposal launch
 
 int32_t launch_accept_dump(const idlm_isd_dims& d, const Plan& p, const void* lc, const void* lm,
                            float T, const char* ws, double* out_p, double* out_q,
