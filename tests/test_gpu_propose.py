@@ -185,8 +185,9 @@ def test_decode_loop_reaches_closed_form(torch_cuda):
     assert abs(tpf - want) < 0.02
 
 
+@pytest.mark.parametrize("B,steps", [(16, 6), (64, 3)])  # one / two sub-chunks per summing WG
 @pytest.mark.parametrize("T", [1.0, 0.0])
-def test_loop_with_mask_stats_matches_plain_acceptance(torch_cuda, T):
+def test_loop_with_mask_stats_matches_plain_acceptance(torch_cuda, T, B, steps):
     """A decode loop over changing logits (clean rows of step t = MASK rows of
     step t-1 plus N(0, 0.5^2), bonus and new MASK rows fresh): the proposals
     record their MASK rows' statistics, and the acceptance of their drafts
@@ -196,9 +197,9 @@ def test_loop_with_mask_stats_matches_plain_acceptance(torch_cuda, T):
     from speculative_verify_isd_amd import lib as L
     from oracle.accept import isd_accept as oracle_accept_batch
 
-    B, N, V, steps, sigma = 16, 4, 151936, 6, 0.5
+    N, V, sigma = 4, 151936, 0.5
     K = N - 1
-    rng = np.random.default_rng(77 + int(T))
+    rng = np.random.default_rng(77 + int(T) + B)
     mask = [rng.normal(0, 3, (B, K, V)).astype(np.float32)]
     clean = [None]
     for t in range(1, steps + 1):
@@ -236,7 +237,7 @@ def test_loop_with_mask_stats_matches_plain_acceptance(torch_cuda, T):
         verified += int((dr[:, 0] >= 0).sum())
         drafts.copy_(nxt)
         lens.copy_(lens_a)
-    print(f"[loop] T={T}: {steps} steps, {verified} verifying sequence-steps, mask-stats "
+    print(f"[loop] B={B} T={T}: {steps} steps, {verified} verifying sequence-steps, mask-stats "
           f"acceptance identical to the plain one and to the oracle", flush=True)
     assert verified >= B  # the record was actually used
 
